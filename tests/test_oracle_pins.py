@@ -1,0 +1,349 @@
+"""Pins of the CPU oracle against things other than itself: exact rational brute force,
+closed forms, textbook/library special cases, invariants and hand-derived bytes.
+
+No GPU.  Each pin is chosen so a plausible mistake in the oracle (a dropped term, a
+flipped sign, a transposed operand, a wrong tie rule or scale axis) fails it; the
+mutation tests at the end plant such mistakes in the oracle and check that a pin fires.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+D = 128
+
+
+def _fp16_codebook(rng, bits):
+    vals = set()
+    while len(vals) < (1 << bits):
+        vals.add(float(np.float16(rng.uniform(-1, 1))))
+    return np.array(sorted(vals), np.float32)
+
+
+# ---------------------------------------------------------------- nearest code ----
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_nearest_code_matches_exact_rational_argmin(bits):
+    """Exact Fraction argmin (ties -> lowest j) agrees with the fp32 scan except where
+    the two best exact distances are within fp32 rounding of each other."""
+    rng = np.random.default_rng(100 + bits)
+    cb = _fp16_codebook(rng, bits)
+    u = rng.uniform(-1.3, 1.3, size=400).astype(np.float32)
+    # adversarial: exact midpoints between neighbours, and points one ulp either side
+    mids = ((cb[:-1].astype(np.float64) + cb[1:]) / 2).astype(np.float32)
+    u = np.concatenate([u, mids, np.nextafter(mids, np.float32(2)), np.nextafter(mids, np.float32(-2)),
+                        cb, np.float32([0.0, -0.0, 1.0, -1.0])]).astype(np.float32)
+    got = oracle.nearest_code(u, cb)
+    for ui, gi in zip(u, got):
+        fu = Fraction(float(ui))
+        dist = [abs(fu - Fraction(float(c))) for c in cb]
+        best = min(range(len(cb)), key=lambda j: (dist[j], j))
+        if gi != best:
+            # an exact tie must go to the lower index; otherwise only an fp32 near-tie
+            # may differ from exact arithmetic
+            assert dist[gi] != dist[best]
+            assert abs(dist[gi] - dist[best]) <= Fraction(2) ** -23 * max(dist[best], Fraction(1, 2 ** 30))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_uniform_codebook_no_outliers_is_textbook_symmetric_uniform(bits):
+    """Uniform codebook, k = 0: value quantization is the textbook symmetric absmax
+    quantizer code = round((x/max|x| + 1)(2^b - 1)/2)."""
+    rng = np.random.default_rng(7 + bits)
+    cb = synth.uniform_codebook(bits)
+    x = rng.standard_normal((64, D)).astype(np.float16)
+    codes, idx, val, s16 = oracle.quantize_values(x, cb, 0)
+    assert idx.shape == (64, 0) and val.shape == (64, 0)
+    s = np.abs(x.astype(np.float64)).max(axis=1)
+    assert np.array_equal(s16.view(np.float16).astype(np.float64), s)
+    levels = (1 << bits) - 1
+    t = (x.astype(np.float64) / s[:, None] + 1.0) * levels / 2.0
+    expect = np.floor(t + 0.5)
+    near_tie = np.abs(t - np.floor(t) - 0.5) < 1e-5
+    assert np.array_equal(codes[~near_tie], expect[~near_tie].astype(np.uint8))
+    # and the reconstruction error is at most half a step
+    deq = oracle.dequant_values(codes, idx, val, s16, cb)
+    # (the fp32-rounded grid levels may overshoot half a step by an fp32 ulp)
+    assert np.all(np.abs(deq - x.astype(np.float64)) <= s[:, None] / levels * (1 + 1e-6))
+
+
+# ------------------------------------------------------------------- outliers ----
+
+def test_outlier_selection_matches_full_sort_with_ties():
+    rng = np.random.default_rng(3)
+    # few distinct magnitudes -> many ties
+    x = rng.choice(np.float16([-3, -2, -1, 0, 1, 2, 3, 2.5, -2.5]), size=(50, D)).astype(np.float16)
+    for k in (0, 1, 2, 5, D):
+        got = oracle.select_outliers(x, k)
+        for r in range(x.shape[0]):
+            order = sorted(range(D), key=lambda c: (-abs(float(x[r, c])), c))
+            assert list(got[r]) == sorted(order[:k])
+
+
+def test_outliers_chosen_by_raw_magnitude_not_scaled():
+    x = np.zeros((1, D), np.float16)
+    x[0, 5] = 8.0     # larger raw magnitude, but a large channel scale
+    x[0, 9] = 3.0     # smaller raw magnitude, small channel scale
+    ks = np.ones(D, np.float32)
+    ks[5] = 100.0
+    codes, idx, val = oracle.quantize_keys(x, ks, synth.uniform_codebook(3), 1)
+    assert list(idx[0]) == [5]
+    assert val[0, 0] == np.float16(8.0).view(np.uint16)
+
+
+def test_key_scale_axis_is_the_channel():
+    """Scaling one channel's scale by 2 while doubling that channel's data leaves its
+    codes unchanged and touches no other channel (per-channel key scale)."""
+    rng = np.random.default_rng(11)
+    cb = _fp16_codebook(rng, 3)
+    x = rng.standard_normal((40, D)).astype(np.float16)
+    ks = np.full(D, 4.0, np.float32)
+    c1, _, _ = oracle.quantize_keys(x, ks, cb, 0)
+    x2 = x.copy()
+    x2[:, 17] = (x2[:, 17].astype(np.float32) * 2).astype(np.float16)
+    ks2 = ks.copy()
+    ks2[17] = 8.0
+    c2, _, _ = oracle.quantize_keys(x2, ks2, cb, 0)
+    assert np.array_equal(c1, c2)
+
+
+def test_value_scale_is_per_vector_max_of_dense_part():
+    rng = np.random.default_rng(12)
+    cb = _fp16_codebook(rng, 3)
+    x = rng.standard_normal((30, D)).astype(np.float16)
+    codes, idx, val, s16 = oracle.quantize_values(x, cb, 2)
+    xf = x.astype(np.float64)
+    for r in range(30):
+        dense = np.delete(xf[r], idx[r].astype(int))
+        assert s16[r] == np.float16(np.abs(dense).max()).view(np.uint16)
+        # the largest dense entry normalises to +-1 -> the end code nearest it
+        c = int(np.delete(np.arange(D), idx[r].astype(int))[np.argmax(np.abs(dense))])
+        end = len(cb) - 1 if xf[r, c] > 0 else 0
+        assert codes[r, c] == end
+
+
+def test_all_zero_dense_part_decodes_to_zero():
+    cb = synth.codebook(0, 3, "v")
+    x = np.zeros((3, D), np.float16)
+    x[:, 4] = 5.0
+    codes, idx, val, s16 = oracle.quantize_values(x, cb, 1)
+    assert np.all(s16.view(np.float16) == 0)
+    assert np.all(codes == oracle.zero_code(cb))
+    deq = oracle.dequant_values(codes, idx, val, s16, cb)
+    expect = np.zeros((3, D))
+    expect[:, 4] = 5.0
+    assert np.array_equal(deq, expect)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_dequant_error_bound(bits):
+    """For dense channels with |u| <= 1: |x~ - x| <= s * max(half the largest codebook
+    gap, distance from the ends to +-1)."""
+    rng = np.random.default_rng(20 + bits)
+    cb = _fp16_codebook(rng, bits)
+    x = rng.standard_normal((200, D)).astype(np.float16)
+    codes, idx, val, s16 = oracle.quantize_values(x, cb, 2)
+    deq = oracle.dequant_values(codes, idx, val, s16, cb)
+    cbd = cb.astype(np.float64)
+    bound = max(np.max(np.diff(cbd)) / 2, 1 - cbd[-1], cbd[0] + 1)
+    s = s16.view(np.float16).astype(np.float64)
+    err = np.abs(deq - x.astype(np.float64))
+    assert np.all(err <= s[:, None] * bound * (1 + 1e-6) + 1e-12)
+    rows = np.arange(200)[:, None]
+    assert np.all(err[rows, idx.astype(int)] == 0)  # outliers exact
+
+
+# ---------------------------------------------------------------------- packing ----
+
+def test_golden_pack_examples():
+    with open(os.path.join(GOLDEN, "pack_examples.json")) as f:
+        g = json.load(f)
+    for ex in g["key_records"]:
+        codes = np.zeros((1, D), np.uint8)
+        for c, v in ex["codes"].items():
+            codes[0, int(c)] = v
+        rec = oracle.pack_key_records(codes, ex["bits"])
+        assert rec.shape == (1, D * ex["bits"] // 8)
+        for byte, v in ex["expect_bytes"].items():
+            assert rec[0, int(byte)] == v, ex["derivation"]
+        assert int(rec.astype(np.int64).sum()) == sum(ex["expect_bytes"].values())
+    for ex in g["value_tiles"]:
+        n = ex["token"] + 1
+        codes = np.zeros((n, D), np.uint8)
+        codes[ex["token"], ex["channel"]] = ex["code"]
+        cap = ((n + 63) // 64) * 64
+        tiles = oracle.pack_value_tiles(codes, ex["bits"], cap)
+        tile = tiles[ex.get("tile", 0)]
+        for byte, v in ex["expect_bytes"].items():
+            assert tile[int(byte)] == v, ex["derivation"]
+        assert int(tile.astype(np.int64).sum()) == sum(ex["expect_bytes"].values())
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_pack_roundtrip(bits):
+    rng = np.random.default_rng(bits)
+    codes = rng.integers(0, 1 << bits, size=(130, D)).astype(np.uint8)
+    rec = oracle.pack_key_records(codes, bits)
+    assert rec.shape == (130, D * bits // 8)
+    assert np.array_equal(oracle.unpack_key_records(rec, bits, D), codes)
+    tiles = oracle.pack_value_tiles(codes, bits, 192)
+    assert tiles.shape == (3, D * 8 * bits)
+    assert np.array_equal(oracle.unpack_value_tiles(tiles, bits, D, 130), codes)
+    # unwritten tail of the last tile is zero
+    assert np.all(oracle.unpack_value_tiles(tiles, bits, D, 192)[130:] == 0)
+
+
+# ------------------------------------------------------------------------- RoPE ----
+
+def _rope_complex(x, pos, base):
+    """Independent formulation: pair (i, i+D/2) as the complex number x_i + j x_{i+D/2},
+    multiplied by exp(j * pos * theta_i) with theta_i = exp(-(2i/D) ln base)."""
+    half = x.shape[1] // 2
+    theta = np.exp(-(2.0 * np.arange(half) / x.shape[1]) * math.log(base))
+    z = (x[:, :half] + 1j * x[:, half:]) * np.exp(1j * np.outer(pos, theta))
+    return np.concatenate([z.real, z.imag], axis=1)
+
+
+def test_rope_matches_complex_rotation_and_invariants():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((40, D))
+    pos = np.concatenate([np.arange(20), rng.integers(0, 2_000_000, size=20)])
+    y = oracle.rope(x, pos, 10000.0)
+    assert np.allclose(y, _rope_complex(x, pos, 10000.0), rtol=0, atol=1e-9)
+    # norm of every rotary pair preserved
+    h = D // 2
+    assert np.allclose(np.hypot(y[:, :h], y[:, h:]), np.hypot(x[:, :h], x[:, h:]), atol=1e-12)
+    # R(0) = I
+    assert np.array_equal(oracle.rope(x, np.zeros(40, int), 10000.0), x)
+    # R(a) R(b) = R(a + b)
+    a, b = 1234, 98765
+    lhs = oracle.rope(oracle.rope(x, np.full(40, a), 1e4), np.full(40, b), 1e4)
+    assert np.allclose(lhs, oracle.rope(x, np.full(40, a + b), 1e4), atol=1e-9)
+    # relative position: R(p)q . R(t)k = q . R(t-p)k
+    q = rng.standard_normal((1, D))
+    p, t = 777, 5000
+    l1 = (oracle.rope(q, [p], 1e4) * oracle.rope(x[:1], [t], 1e4)).sum()
+    l2 = (q * oracle.rope(x[:1], [t - p], 1e4)).sum()
+    assert abs(l1 - l2) < 1e-9
+
+
+def test_rope_frequencies_closed_form():
+    th = oracle.rope_frequencies(D, 10000.0)
+    assert th[0] == 1.0
+    assert np.allclose(th, 10000.0 ** (-np.arange(64) / 64.0), rtol=1e-15)
+    assert np.all(np.diff(th) < 0)
+
+
+# ------------------------------------------------------------------- attention ----
+
+def _exact_attention(q, k16, v16, base, sm):
+    """Textbook attention on the unquantized fp16 K/V: complex-rotated keys and
+    torch's scaled_dot_product_attention in float64."""
+    kr = _rope_complex(k16.astype(np.float64), np.arange(k16.shape[0]), base)
+    qt = torch.tensor(q, dtype=torch.float64).view(1, 1, 1, -1)
+    kt = torch.tensor(kr).view(1, 1, -1, k16.shape[1])
+    vt = torch.tensor(v16.astype(np.float64)).view(1, 1, -1, k16.shape[1])
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=sm)
+    logits = sm * (kr @ q)
+    return logits, out.view(-1).numpy()
+
+
+def test_all_outliers_is_exact_attention():
+    """k = D: every entry is kept in fp16, so decode attention over the compressed cache
+    is exact attention over the fp16 keys and values."""
+    wl = synth.WORKLOADS["single_head_4k"]
+    n = 300
+    k16 = synth.keys(1, wl, 0, 0, n).numpy()
+    v16 = synth.values(1, wl, 0, 0, n).numpy()
+    ks = synth.key_scale(1, wl)[0]
+    cbk, cbv = synth.codebook(1, 3, "k"), synth.codebook(1, 3, "v")
+    cache = oracle.quantize_stream(k16, v16, ks, cbk, cbv, D)
+    q = synth.queries(1, wl)[0, 0].numpy().astype(np.float64)
+    sm = 1 / math.sqrt(D)
+    logits, out = oracle.decode_head(q, cache, ks, cbk, cbv, 1e4, sm)
+    el, eo = _exact_attention(q, k16, v16, 1e4, sm)
+    assert np.allclose(logits, el, rtol=0, atol=1e-10)
+    assert np.allclose(out, eo, rtol=0, atol=1e-12)
+
+
+def test_softmax_shift_invariance_and_special_cases():
+    rng = np.random.default_rng(9)
+    l = rng.standard_normal(50) * 5
+    v = rng.standard_normal((50, D))
+    assert np.allclose(oracle.attend(l, v), oracle.attend(l + 123.0, v), atol=1e-13)
+    assert np.allclose(oracle.attend(np.zeros(50), v), v.mean(axis=0), atol=1e-13)
+    assert np.allclose(oracle.attend(l[:1], v[:1]), v[0], atol=0)
+
+
+def test_split_softmax_combine_equals_single_pass():
+    """The log-sum-exp merge of per-chunk (max, sum, weighted sum) partials equals the
+    single-pass softmax product, for any chunking (the split-K identity)."""
+    rng = np.random.default_rng(10)
+    l = rng.standard_normal(1000) * 4
+    v = rng.standard_normal((1000, D))
+    ref = oracle.attend(l, v)
+    for chunk in (1, 7, 64, 333, 1000):
+        ms, ss, os_ = [], [], []
+        for s in range(0, 1000, chunk):
+            lc = l[s:s + chunk]
+            m = lc.max()
+            p = np.exp(lc - m)
+            ms.append(m); ss.append(p.sum()); os_.append(p @ v[s:s + chunk])
+        M = max(ms)
+        w = np.exp(np.array(ms) - M)
+        out = (w[:, None] * np.array(os_)).sum(0) / (w * np.array(ss)).sum()
+        assert np.allclose(out, ref, atol=1e-13)
+
+
+# ------------------------------------------------------------- planted mistakes ----
+
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """Plant plausible mistakes in the oracle (CPU only) and check a pin fires."""
+    # 1. RoPE with a flipped sine
+    good_rope = oracle.kvquant.rope
+
+    def bad_rope(x, positions, base):
+        y = good_rope(x, positions, base)
+        h = y.shape[1] // 2
+        xx = np.asarray(x, np.float64)
+        phi = np.asarray(positions, np.float64)[:, None] * oracle.rope_frequencies(x.shape[1], base)
+        return np.concatenate([xx[:, :h] * np.cos(phi) + xx[:, h:] * np.sin(phi), y[:, h:]], axis=1)
+
+    monkeypatch.setattr(oracle.kvquant, "rope", bad_rope)
+    with pytest.raises(AssertionError):
+        test_all_outliers_is_exact_attention()
+    monkeypatch.setattr(oracle.kvquant, "rope", good_rope)
+
+    # 2. outliers dropped from the decode (sparse term lost)
+    good_scatter = oracle.kvquant._scatter_outliers
+    monkeypatch.setattr(oracle.kvquant, "_scatter_outliers", lambda x, i, v: x)
+    with pytest.raises(AssertionError):
+        test_all_outliers_is_exact_attention()
+    monkeypatch.setattr(oracle.kvquant, "_scatter_outliers", good_scatter)
+
+    # 3. key fields stored in channel order instead of rotary-pair order
+    good_fields = oracle.kvquant.key_field_channels
+    monkeypatch.setattr(oracle.kvquant, "key_field_channels", lambda d: np.arange(d))
+    with pytest.raises(AssertionError):
+        test_golden_pack_examples()
+    monkeypatch.setattr(oracle.kvquant, "key_field_channels", good_fields)
+
+    # 4. nearest-code ties resolved toward the higher index
+    good_nc = oracle.kvquant.nearest_code
+
+    def bad_nc(u, cb):
+        cbr = np.asarray(cb)[::-1]
+        return (len(cbr) - 1 - good_nc(u, cbr)).astype(np.uint8)
+
+    monkeypatch.setattr(oracle, "nearest_code", bad_nc)
+    with pytest.raises(AssertionError):
+        test_nearest_code_matches_exact_rational_argmin(3)
+    monkeypatch.setattr(oracle, "nearest_code", good_nc)
