@@ -1,0 +1,241 @@
+"""Benchmark: quantized-KV decode attention on one MI355X.
+
+A step is one decode step of a whole LLaMA-7B-shaped model at 32K context: for each of
+the model's layers, kvq_quantize_append of the new token's key and value, then
+kvq_qk_matvec and kvq_pv_matvec over that layer's compressed cache.  Every layer has its
+own cache (different seeded inputs), so a step reads ~3.7 GB of compressed KV and no
+layer's cache is still resident in the 256 MB last-level cache when it is read again.
+
+Prints ONE JSON line.  value = algorithmic HBM bytes per step / step time (GB/s).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="llama7b_32k")
+    p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-heads", type=int, default=24, help="kv-head streams the oracle times in the CPU leg")
+    return p.parse_args()
+
+
+def algorithmic_bytes(wl, L):
+    """Bytes one layer's kernels must move at cache length L (per step)."""
+    k = wl.n_outliers
+    tok_heads = wl.batch * wl.n_kv_heads * L
+    q_tok = wl.batch * wl.n_q_heads * L
+    qk = tok_heads * (wl.head_dim * wl.k_bits // 8 + 3 * k) + q_tok * 4  # K records + outliers, logits write
+    pv = tok_heads * (wl.head_dim * wl.v_bits // 8 + 3 * k + 2) + q_tok * 4  # V tiles + outliers + scale, logits read
+    # append: read 2 fp16 vectors, write one key record, read-modify-write one value tile,
+    # outliers and scale, per (sequence, kv head)
+    nvec = wl.batch * wl.n_kv_heads * wl.n_new
+    app = nvec * (2 * wl.head_dim * 2 + wl.head_dim * wl.k_bits // 8 + 2 * 1024 * wl.v_bits + 6 * k + 2)
+    return qk, pv, app
+
+
+def source_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "long_context_decode_kvq_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel, src_hash):
+    """HBM bytes per launch measured with rocprofv3 counters, if the committed
+    measurement was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get(kernel)
+    if not e or e.get("source_hash") != src_hash:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, seed, n_heads):
+    """Time the oracle (as it stands) on a bounded sample of the same step: the decode-step
+    append and full-length decode attention for n_heads (sequence, kv head) streams of
+    layer 0; report the rate scaled to algorithmic bytes per second."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import synth
+
+    L = wl.seq_len
+    sm = 1.0 / math.sqrt(wl.head_dim)
+    ks = synth.key_scale(seed, wl)
+    cbk, cbv = synth.codebook(seed, wl.k_bits, "k"), synth.codebook(seed, wl.v_bits, "v")
+    q = synth.queries(seed, wl)
+    elapsed = 0.0
+    with threadpool_limits(limits=1):
+        torch.set_num_threads(1)
+        for h in range(n_heads):
+            kx = synth.keys(seed, wl, 0, h, L + 1).numpy()
+            vx = synth.values(seed, wl, 0, h, L + 1).numpy()
+            cache = oracle.quantize_stream(kx[:L], vx[:L], ks[h], cbk, cbv, wl.n_outliers)  # prefix: not timed
+            t0 = time.perf_counter()
+            new = oracle.quantize_stream(kx[L:], vx[L:], ks[h], cbk, cbv, wl.n_outliers)
+            full = oracle.StreamCache(*(np.concatenate([a, b]) for a, b in zip(
+                (cache.k_codes, cache.k_idx, cache.k_val, cache.v_codes, cache.v_idx, cache.v_val, cache.v_scale),
+                (new.k_codes, new.k_idx, new.k_val, new.v_codes, new.v_idx, new.v_val, new.v_scale))))
+            oracle.pack_key_records(new.k_codes, wl.k_bits)
+            for hq in range(h * wl.group, (h + 1) * wl.group):
+                oracle.decode_head(q[0, hq].float().numpy().astype(np.float64), full, ks[h], cbk, cbv,
+                                   wl.rope_base, sm)
+            elapsed += time.perf_counter() - t0
+    qk, pv, app = algorithmic_bytes(wl, L + 1)
+    per_stream = (qk + pv + app) / (wl.batch * wl.n_kv_heads)
+    return {"value": round(per_stream * n_heads / elapsed / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n_heads} of {wl.batch * wl.n_kv_heads} kv-head streams of one layer, L={L + 1}: "
+                      f"append of the new token + float64 decode attention, {elapsed:.1f} s, 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                          "(sharding across GPUs is designed, not built)"}))
+        sys.exit(2)
+    import torch
+
+    import long_context_decode_kvq_amd as kvq
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = "cuda"
+    kvq.load_library()
+    L0 = wl.seq_len
+    total_new = (args.warmup + args.steps) * wl.n_new
+    max_seq = ((L0 + total_new + 63) // 64) * 64
+    cfg = kvq.CacheConfig(wl.batch, wl.n_q_heads, wl.n_kv_heads, max_seq, wl.k_bits, wl.v_bits, wl.n_outliers,
+                          wl.head_dim, wl.rope_base)
+
+    # ---- build one cache per layer (prefill through kvq_quantize_append) --------------
+    layers = []
+    for li in range(args.layers):
+        s = args.seed * 1000 + li
+        ks = torch.from_numpy(synth.key_scale(s, wl))
+        cache = kvq.KVCache(cfg, ks, torch.from_numpy(synth.codebook(s, wl.k_bits, "k")),
+                            torch.from_numpy(synth.codebook(s, wl.v_bits, "v")), dev)
+        n_all = L0 + total_new
+        kraw = torch.empty(wl.batch, n_all, wl.n_kv_heads, wl.head_dim, dtype=torch.float16, device=dev)
+        vraw = torch.empty_like(kraw)
+        for b in range(wl.batch):
+            for h in range(wl.n_kv_heads):
+                kraw[b, :, h] = synth.keys(s, wl, b, h, n_all, dev)
+                vraw[b, :, h] = synth.values(s, wl, b, h, n_all, dev)
+        kvq.quantize_append(cache, kraw[:, :L0].contiguous(), vraw[:, :L0].contiguous())
+        new_k = [kraw[:, L0 + i * wl.n_new: L0 + (i + 1) * wl.n_new].contiguous() for i in range(total_new // wl.n_new)]
+        new_v = [vraw[:, L0 + i * wl.n_new: L0 + (i + 1) * wl.n_new].contiguous() for i in range(total_new // wl.n_new)]
+        del kraw, vraw
+        layers.append(dict(cache=cache, q=synth.queries(s, wl, dev), bufs=kvq.DecodeBuffers(cache),
+                           new_k=new_k, new_v=new_v))
+        torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    kern_events = {"qk": [], "pv": []}
+
+    def step(i, record):
+        for lay in layers:
+            c = lay["cache"]
+            kvq.quantize_append(c, lay["new_k"][i], lay["new_v"][i])
+            L = max(c.lengths)
+            if record:
+                e0, e1, e2 = ev(), ev(), ev()
+                e0.record()
+            kvq.qk_matvec(c, lay["q"], lay["bufs"].logits, max_len=L)
+            if record:
+                e1.record()
+            kvq.pv_matvec(c, lay["bufs"].logits, lay["bufs"].out, lay["bufs"].workspace, max_len=L)
+            if record:
+                e2.record()
+                kern_events["qk"].append((e0, e1))
+                kern_events["pv"].append((e1, e2))
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    start_len = max(layers[0]["cache"].lengths)
+    t_start, t_end = ev(), ev()
+    w0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+
+    # bytes: lengths grow by n_new per step; use the mean length over the timed steps
+    L_mean = start_len + wl.n_new * (args.steps + 1) / 2.0
+    qk_b, pv_b, app_b = algorithmic_bytes(wl, L_mean)
+    step_bytes = args.layers * (qk_b + pv_b + app_b)
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    kv_tok_s = args.layers * wl.batch * L_mean / (ms_step * 1e-3)
+
+    kt = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in kern_events.items()}  # ms per launch
+    dom = max(kt, key=kt.get)
+    dom_bytes = {"qk": qk_b, "pv": pv_b}[dom]
+    achieved = dom_bytes / (kt[dom] * 1e-3) / 1e9
+    src = {"qk": ["qk.hip", "kvq_device.h"], "pv": ["pv.hip", "kvq_device.h"]}[dom]
+    traffic = traffic_from_profile(dom, source_hash(src))
+
+    line = {
+        "metric": "quantized-KV decode attention: achieved HBM GB/s (% of peak) + KV-tokens/s",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) keys with 4 x10 channels, N(0,1) values; fp16 queries)",
+        "config": {"workload": args.workload, "layers": args.layers, "batch": wl.batch,
+                   "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
+                   "seq_len": wl.seq_len, "k_bits": wl.k_bits, "v_bits": wl.v_bits,
+                   "outliers_per_vector": wl.n_outliers, "new_tokens_per_step": wl.n_new},
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "kv_tokens_per_s": round(kv_tok_s, 1),
+        "kernel_ms": {k: round(v, 5) for k, v in kt.items()},
+        "kernel_gbs": {"qk": round(qk_b / (kt["qk"] * 1e-3) / 1e9, 1),
+                       "pv": round(pv_b / (kt["pv"] * 1e-3) / 1e9, 1)},
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"kernel": {"qk": "qk_kernel", "pv": "pv_partial_kernel+pv_combine_kernel"}[dom],
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.seed * 1000, args.cpu_heads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

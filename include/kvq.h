@@ -1,0 +1,162 @@
+/*
+ * kvq.h - C ABI of the quantized-KV decode-attention library (libkvq.so), gfx950.
+ *
+ * The library implements the decode hot path of KVQuant ("KVQuant: Towards 10 Million
+ * Context Length LLM Inference with KV Cache Quantization", study.space summary,
+ * abstract paragraph; and the phantomic12 paper note, "Four components" paragraph):
+ *   (i)   keys are quantized per channel,
+ *   (ii)  keys are quantized before the rotary embedding, which is applied after
+ *         dequantization at each cached token's own position,
+ *   (iii) every entry is mapped to the nearest entry of a sorted per-layer
+ *         non-uniform codebook of 2^b values in [-1, 1],
+ *   (iv)  each (token, kv head) vector keeps its k largest-magnitude entries aside in
+ *         fp16 (dense-and-sparse split), the rest is quantized.
+ * Decode is memory-bound (summary page, same paragraph): every kernel here streams the
+ * compressed cache once.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates nothing and keeps no state between calls.
+ *   - fp16 data is passed as uint16_t bit patterns.
+ *   - Work is enqueued on `stream` and returns without synchronising.  Host-checkable
+ *     errors return a negative kvq_status and enqueue nothing.  A failed launch returns
+ *     KVQ_ERR_HIP.  Faults inside a kernel surface at the caller's next synchronisation.
+ *   - Inputs must be finite (no NaN/Inf keys or values).
+ *
+ * Storage layout of the compressed cache (B = batch, H = n_kv_heads, S = max_seq, a
+ * multiple of 64, D = head_dim = 128, k = n_outliers):
+ *   k_codes   uint8 [B][H][S][D*k_bits/8]      one record per token.  Field f (b bits)
+ *             holds channel f/2 + (D/2)*(f%2), i.e. the two halves of each rotary pair
+ *             side by side; bit i of field f is stream bit f*b+i; stream bit p is bit
+ *             p%8 of byte p/8 (little-endian bitstream).
+ *   v_codes   uint8 [B][H][S/64][D*8*v_bits]   channel-major 64-token tiles: inside a
+ *             tile, channel c owns bytes [c*8*b, (c+1)*8*b): its 64 codes in token order
+ *             as a little-endian bitstream.
+ *   k_out_idx uint8  [B][H][S][k]  outlier channels of each key vector, ascending
+ *   k_out_val uint16 [B][H][S][k]  their fp16 values, unchanged
+ *   v_out_idx, v_out_val           the same for values
+ *   v_scale   uint16 [B][H][S]     fp16 per-vector value scale (max |dense entry|)
+ *   k_scale   float  [H][D]        frozen per-channel key scale (caller calibrated)
+ *   k_codebook, v_codebook  float [2^bits], strictly ascending, in [-1, 1]
+ *   seq_len   int32 [B]            tokens held per sequence (device copy)
+ * Bits of tokens at or beyond seq_len[b] are never read.  A cache whose buffers start
+ * zero-filled holds zero bits there, which makes the packed buffers comparable byte for
+ * byte.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID = -1,      /* null pointer, negative or inconsistent size */
+  KVQ_ERR_UNSUPPORTED = -2,  /* head_dim != 128, bits not in {2,3,4}, group not in {1,2,4,8} */
+  KVQ_ERR_CAPACITY = -3,     /* an append would pass max_seq */
+  KVQ_ERR_WORKSPACE = -4,    /* workspace null or smaller than kvq_workspace_bytes() */
+  KVQ_ERR_HIP = -5           /* a HIP launch or runtime call failed */
+} kvq_status;
+
+typedef struct {
+  int32_t batch;       /* B >= 1 */
+  int32_t n_q_heads;   /* Hq, a multiple of n_kv_heads; q head h reads kv head h / (Hq/Hkv) */
+  int32_t n_kv_heads;  /* Hkv >= 1 */
+  int32_t head_dim;    /* D, must be 128 */
+  int32_t max_seq;     /* S, cache capacity in tokens, a positive multiple of 64 */
+  int32_t k_bits;      /* 2, 3 or 4 */
+  int32_t v_bits;      /* 2, 3 or 4 */
+  int32_t n_outliers;  /* k per (token, kv head) vector, 0 <= k <= D */
+  float rope_base;     /* rotary base (10000 for LLaMA-family models), > 1 */
+} kvq_shape;
+
+typedef struct {
+  uint8_t *k_codes, *v_codes;
+  uint8_t *k_out_idx;
+  uint16_t *k_out_val;
+  uint8_t *v_out_idx;
+  uint16_t *v_out_val;
+  uint16_t *v_scale;
+  const float *k_scale;
+  const float *k_codebook, *v_codebook;
+  int32_t *seq_len;
+} kvq_cache;
+
+/* Byte sizes of each cache buffer for `shape` (host only, no device work). */
+typedef struct {
+  size_t k_codes, v_codes, k_out_idx, k_out_val, v_out_idx, v_out_val, v_scale;
+  size_t k_scale, k_codebook, v_codebook, seq_len;
+  size_t total;  /* sum of all of the above */
+} kvq_sizes;
+
+int kvq_cache_sizes(const kvq_shape* shape, kvq_sizes* out);
+
+/* Workspace bytes kvq_pv_matvec needs for caches of at most `max_len` tokens.
+ * Returns 0 for an invalid shape or max_len < 1. */
+size_t kvq_workspace_bytes(const kvq_shape* shape, int32_t max_len);
+
+/*
+ * Quantize and append new keys/values (summary page, techniques (i)-(iv)).
+ *   k_new, v_new   fp16 [B][n_max][Hkv][D], keys BEFORE the rotary embedding.
+ *   n_max          tokens per sequence in k_new / v_new (>= 0).
+ *   n_new_host     host int32 [B]: tokens of sequence b to append (its first n_new_host[b]
+ *                  rows, 0 <= n_new_host[b] <= n_max); NULL appends n_max for every b.
+ *   seq_len_host   host int32 [B]: current length of every sequence (must equal the
+ *                  device seq_len).  Token j of sequence b goes to position
+ *                  seq_len_host[b] + j.
+ * Per new vector: the k largest |x| entries (ties to the lower channel) go to the outlier
+ * store in ascending channel order with their fp16 bits; the dense rest (outlier slots
+ * zeroed) is divided in float32 by the key's per-channel scale or by the value vector's
+ * own max |dense| (0 -> all-zero u) and coded as the lowest j minimising |u - cb_j|.
+ * Afterwards seq_len[b] = seq_len_host[b] + n_new (device), enqueued on `stream`.
+ * Errors: KVQ_ERR_CAPACITY if any seq_len_host[b] + n_new > max_seq.
+ */
+int kvq_quantize_append(const kvq_shape* shape, const kvq_cache* cache, const uint16_t* k_new,
+                        const uint16_t* v_new, int32_t n_max, const int32_t* n_new_host,
+                        const int32_t* seq_len_host, hipStream_t stream);
+
+/*
+ * Decode-time q.K^T over the compressed key cache (paper note, item (2): RoPE after
+ * dequantization).
+ *   q          [B][Hq][D], float32 (q_is_fp16 = 0) or fp16 bits (q_is_fp16 = 1), already
+ *              rotated at the query's own position.
+ *   logits     float32 [B][Hq][max_seq]; for every t < seq_len[b]:
+ *              logits[b][h][t] = sm_scale * q[b][h] . RoPE_t(k~[b][h/g][t]),
+ *              k~ = cb_K[code] * k_scale (dense channels) or the fp16 outlier value;
+ *              RoPE_t rotates pair (i, i+D/2) by t * rope_base^(-2i/D).
+ *              Entries at t >= seq_len[b] are not written.
+ *   max_len    host bound, >= every seq_len[b] and <= max_seq; sizes the grid.
+ */
+int kvq_qk_matvec(const kvq_shape* shape, const kvq_cache* cache, const void* q, int32_t q_is_fp16,
+                  float sm_scale, float* logits, int32_t max_len, hipStream_t stream);
+
+/*
+ * softmax(logits) . V over the compressed value cache plus the value outliers, as a
+ * split over the sequence (chunks of tokens) followed by a log-sum-exp combine.
+ *   logits     float32 [B][Hq][max_seq] as written by kvq_qk_matvec.
+ *   out        float32 [B][Hq][D]: sum_t p_t v~[b][h/g][t], p = softmax over t < seq_len[b];
+ *              a sequence of length 0 gives zeros.
+ *   workspace  device scratch of at least kvq_workspace_bytes(shape, max_len) bytes.
+ */
+int kvq_pv_matvec(const kvq_shape* shape, const kvq_cache* cache, const float* logits, float* out,
+                  void* workspace, size_t workspace_bytes, int32_t max_len, hipStream_t stream);
+
+/* Human-readable name of a kvq_status value (static string). */
+const char* kvq_status_string(int status);
+
+/* ABI version of this header (bumped on any incompatible change). */
+int kvq_abi_version(void);
+
+#define KVQ_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,199 @@
+// Online quantize-append of new key/value vectors into the compressed cache.
+//
+// KVQuant summary page, abstract paragraph, techniques (i)-(iv): per-channel key scale,
+// keys taken before the rotary embedding, nearest entry of a sorted per-layer
+// non-uniform codebook, and per-vector dense-and-sparse outlier isolation.
+//
+// One wave owns one (sequence, kv head, 64-token tile) and walks the new tokens that
+// fall into that tile in order, so the read-modify-write of the channel-major value
+// tile has a single writer.  Inside the wave a vector's 128 channels sit two per lane:
+// keys as (l, l + 64) -- the two halves of rotary pair l, adjacent in the key record --
+// and values as (2l, 2l + 1), which is how the value tile stores them.
+#include <type_traits>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+// Selection key: fp16 magnitude bits above the inverted channel index, so the unsigned
+// maximum is the largest |x| and, among equal magnitudes, the lowest channel.
+__device__ __forceinline__ uint32_t outlier_key(uint32_t xbits, uint32_t c) {
+  return ((xbits & 0x7fffu) << 16) | (0xffffu - c);
+}
+
+// Marks the k largest-magnitude channels of the wave's vector (k <= 128).
+__device__ __forceinline__ void select_outliers(uint32_t key0, uint32_t key1, int k, bool& sel0,
+                                                bool& sel1) {
+  sel0 = false;
+  sel1 = false;
+  for (int r = 0; r < k; ++r) {
+    uint32_t m0 = sel0 ? 0u : key0;
+    uint32_t m1 = sel1 ? 0u : key1;
+    uint32_t m = wave_max_u32(m0 > m1 ? m0 : m1);
+    if (!sel0 && key0 == m) {
+      sel0 = true;
+    } else if (!sel1 && key1 == m) {
+      sel1 = true;
+    }
+  }
+}
+
+template <int KB, int VB>
+__global__ __launch_bounds__(64) void append_kernel(AppendArgs a) {
+  constexpr int kNcK = 1 << KB;
+  constexpr int kNcV = 1 << VB;
+  constexpr int kRecWords = 4 * KB;    // key record: D*KB/8 bytes
+  constexpr int kLaneWords = 4 * VB;   // value tile bytes owned by one lane (2 channels)
+  constexpr int kChanWords = 2 * VB;   // one channel's 64 codes
+
+  __shared__ float cbk[kNcK];
+  __shared__ float cbv[kNcV];
+  __shared__ uint32_t rec[kRecWords];
+  __shared__ uint32_t vt[kWave * kLaneWords];
+
+  const int lane = threadIdx.x;
+  const int seq = blockIdx.z;
+  const int kvh = blockIdx.y;
+  const int start = a.start[seq];
+  const int count = a.count[seq];
+  const int H = a.n_kv_heads;
+  const int S = a.max_seq;
+  const int k = a.n_outliers;
+
+  if (blockIdx.x == 0 && kvh == 0 && lane == 0) a.seq_len[seq] = start + count;
+
+  const int tile = start / kTile + blockIdx.x;
+  const int lo = max(start, tile * kTile);
+  const int hi = min(start + count, (tile + 1) * kTile);
+  if (lo >= hi) return;
+
+  if (lane < kNcK) cbk[lane] = a.k_cb[lane];
+  if (lane < kNcV) cbv[lane] = a.v_cb[lane];
+
+  const size_t stream = static_cast<size_t>(seq) * H + kvh;
+  uint32_t* vtile = reinterpret_cast<uint32_t*>(a.v_codes + (stream * (S / kTile) + tile) * (1024 * VB));
+  for (int i = lane; i < kWave * kLaneWords; i += kWave) vt[i] = vtile[i];
+
+  const float ks0 = a.k_scale[kvh * kHeadDim + lane];
+  const float ks1 = a.k_scale[kvh * kHeadDim + lane + kHalf];
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  __syncthreads();
+
+  for (int t = lo; t < hi; ++t) {
+    const int j = t - start;  // row of this token in the new-token block
+    const size_t src = ((static_cast<size_t>(seq) * a.n_max + j) * H + kvh) * kHeadDim;
+    const size_t slot = stream * S + t;
+
+    // ---- key: channels (lane, lane + 64), per-channel scale ------------------------
+    {
+      const uint32_t x0 = a.k_new[src + lane];
+      const uint32_t x1 = a.k_new[src + lane + kHalf];
+      bool sel0, sel1;
+      select_outliers(outlier_key(x0, lane), outlier_key(x1, lane + kHalf), k, sel0, sel1);
+      const uint64_t b0 = __ballot(sel0);
+      const uint64_t b1 = __ballot(sel1);
+      if (sel0) {
+        const int r = __popcll(b0 & lt);
+        a.k_idx[slot * k + r] = static_cast<uint8_t>(lane);
+        a.k_val[slot * k + r] = static_cast<uint16_t>(x0);
+      }
+      if (sel1) {
+        const int r = __popcll(b0) + __popcll(b1 & lt);
+        a.k_idx[slot * k + r] = static_cast<uint8_t>(lane + kHalf);
+        a.k_val[slot * k + r] = static_cast<uint16_t>(x1);
+      }
+      const float d0 = sel0 ? 0.0f : half_bits_to_float(x0);
+      const float d1 = sel1 ? 0.0f : half_bits_to_float(x1);
+      const float u0 = ks0 > 0.0f ? d0 / ks0 : 0.0f;
+      const float u1 = ks1 > 0.0f ? d1 / ks1 : 0.0f;
+      const uint32_t pair = nearest_code<kNcK>(u0, cbk) | (nearest_code<kNcK>(u1, cbk) << KB);
+      if (lane < kRecWords) rec[lane] = 0u;
+      __syncthreads();
+      const int bit = 2 * KB * lane;
+      const int w = bit >> 5;
+      const int sh = bit & 31;
+      atomicOr(&rec[w], pair << sh);
+      if (sh + 2 * KB > 32) atomicOr(&rec[w + 1], pair >> (32 - sh));
+      __syncthreads();
+      if (lane < kRecWords) reinterpret_cast<uint32_t*>(a.k_codes + slot * (16 * KB))[lane] = rec[lane];
+    }
+
+    // ---- value: channels (2 lane, 2 lane + 1), one scale per vector ----------------
+    {
+      const uint32_t xx = reinterpret_cast<const uint32_t*>(a.v_new + src)[lane];
+      const uint32_t x0 = xx & 0xffffu;
+      const uint32_t x1 = xx >> 16;
+      bool sel0, sel1;
+      select_outliers(outlier_key(x0, 2 * lane), outlier_key(x1, 2 * lane + 1), k, sel0, sel1);
+      const uint64_t b0 = __ballot(sel0);
+      const uint64_t b1 = __ballot(sel1);
+      const int r0 = __popcll(b0 & lt) + __popcll(b1 & lt);
+      if (sel0) {
+        a.v_idx[slot * k + r0] = static_cast<uint8_t>(2 * lane);
+        a.v_val[slot * k + r0] = static_cast<uint16_t>(x0);
+      }
+      if (sel1) {
+        const int r1 = r0 + (sel0 ? 1 : 0);
+        a.v_idx[slot * k + r1] = static_cast<uint8_t>(2 * lane + 1);
+        a.v_val[slot * k + r1] = static_cast<uint16_t>(x1);
+      }
+      const uint32_t m0 = sel0 ? 0u : (x0 & 0x7fffu);
+      const uint32_t m1 = sel1 ? 0u : (x1 & 0x7fffu);
+      const uint32_t sbits = wave_max_u32(m0 > m1 ? m0 : m1);
+      const float s = half_bits_to_float(sbits);
+      if (lane == 0) a.v_scale[slot] = static_cast<uint16_t>(sbits);
+      const float d0 = sel0 ? 0.0f : half_bits_to_float(x0);
+      const float d1 = sel1 ? 0.0f : half_bits_to_float(x1);
+      const float u0 = s > 0.0f ? d0 / s : 0.0f;
+      const float u1 = s > 0.0f ? d1 / s : 0.0f;
+      const uint32_t c0 = nearest_code<kNcV>(u0, cbv);
+      const uint32_t c1 = nearest_code<kNcV>(u1, cbv);
+      const int tau = t - tile * kTile;
+      const int bit = tau * VB;
+      const int w = bit >> 5;
+      const int sh = bit & 31;
+      constexpr uint32_t mask = (1u << VB) - 1u;
+      uint32_t* seg = vt + lane * kLaneWords;
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        const uint32_t code = ch ? c1 : c0;
+        uint32_t* cw = seg + ch * kChanWords;
+        cw[w] = (cw[w] & ~(mask << sh)) | (code << sh);
+        if (sh + VB > 32) cw[w + 1] = (cw[w + 1] & ~(mask >> (32 - sh))) | (code >> (32 - sh));
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = lane; i < kWave * kLaneWords; i += kWave) vtile[i] = vt[i];
+}
+
+template <int KB, int VB>
+hipError_t launch_append_t(const AppendArgs& a, hipStream_t s) {
+  int max_tiles = 0;
+  for (int b = 0; b < a.n_batch; ++b) {
+    if (a.count[b] > 0) {
+      const int first = a.start[b] / kTile;
+      const int last = (a.start[b] + a.count[b] - 1) / kTile;
+      max_tiles = max(max_tiles, last - first + 1);
+    }
+  }
+  dim3 grid(max(max_tiles, 1), a.n_kv_heads, a.n_batch);
+  hipLaunchKernelGGL((append_kernel<KB, VB>), grid, dim3(kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append(int k_bits, int v_bits, const AppendArgs& a, hipStream_t s) {
+#define KVQ_APPEND_CASE(KB, VB) \
+  if (k_bits == KB && v_bits == VB) return launch_append_t<KB, VB>(a, s);
+  KVQ_APPEND_CASE(2, 2) KVQ_APPEND_CASE(2, 3) KVQ_APPEND_CASE(2, 4)
+  KVQ_APPEND_CASE(3, 2) KVQ_APPEND_CASE(3, 3) KVQ_APPEND_CASE(3, 4)
+  KVQ_APPEND_CASE(4, 2) KVQ_APPEND_CASE(4, 3) KVQ_APPEND_CASE(4, 4)
+#undef KVQ_APPEND_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

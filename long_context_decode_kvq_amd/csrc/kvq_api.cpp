@@ -1,0 +1,203 @@
+// C ABI of libkvq.so: argument validation, sizing, and kernel dispatch.
+// Every check that the host can make is made before anything is enqueued.
+#include "../../include/kvq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace {
+
+bool bits_ok(int b) { return b == 2 || b == 3 || b == 4; }
+bool group_ok(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+int check_shape(const kvq_shape* s) {
+  if (!s) return KVQ_ERR_INVALID;
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->max_seq < 1) return KVQ_ERR_INVALID;
+  if (s->max_seq % kvq::kTile != 0) return KVQ_ERR_INVALID;
+  if (s->n_q_heads % s->n_kv_heads != 0) return KVQ_ERR_INVALID;
+  if (s->n_outliers < 0) return KVQ_ERR_INVALID;
+  if (!(s->rope_base > 1.0f) || !std::isfinite(s->rope_base)) return KVQ_ERR_INVALID;
+  if (s->head_dim != kvq::kHeadDim) return KVQ_ERR_UNSUPPORTED;
+  if (s->n_outliers > s->head_dim) return KVQ_ERR_INVALID;
+  if (!bits_ok(s->k_bits) || !bits_ok(s->v_bits)) return KVQ_ERR_UNSUPPORTED;
+  if (!group_ok(s->n_q_heads / s->n_kv_heads)) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+int check_cache_common(const kvq_shape* s, const kvq_cache* c) {
+  if (!c) return KVQ_ERR_INVALID;
+  if (!c->seq_len) return KVQ_ERR_INVALID;
+  if (s->n_outliers > 0) {
+    if (!c->k_out_idx || !c->k_out_val || !c->v_out_idx || !c->v_out_val) return KVQ_ERR_INVALID;
+  }
+  return KVQ_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+size_t n_chunks_for(int32_t max_len) { return (static_cast<size_t>(max_len) + kvq::kPvChunk - 1) / kvq::kPvChunk; }
+
+}  // namespace
+
+extern "C" {
+
+int kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char* kvq_status_string(int status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported shape or bit width";
+    case KVQ_ERR_CAPACITY: return "append exceeds cache capacity";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int kvq_cache_sizes(const kvq_shape* s, kvq_sizes* out) {
+  int st = check_shape(s);
+  if (st != KVQ_OK) return st;
+  if (!out) return KVQ_ERR_INVALID;
+  const size_t streams = static_cast<size_t>(s->batch) * s->n_kv_heads;
+  const size_t slots = streams * s->max_seq;
+  const size_t D = s->head_dim;
+  kvq_sizes z;
+  std::memset(&z, 0, sizeof(z));
+  z.k_codes = slots * D * s->k_bits / 8;
+  z.v_codes = slots * D * s->v_bits / 8;
+  z.k_out_idx = slots * s->n_outliers;
+  z.k_out_val = slots * s->n_outliers * 2;
+  z.v_out_idx = slots * s->n_outliers;
+  z.v_out_val = slots * s->n_outliers * 2;
+  z.v_scale = slots * 2;
+  z.k_scale = static_cast<size_t>(s->n_kv_heads) * D * 4;
+  z.k_codebook = (static_cast<size_t>(1) << s->k_bits) * 4;
+  z.v_codebook = (static_cast<size_t>(1) << s->v_bits) * 4;
+  z.seq_len = static_cast<size_t>(s->batch) * 4;
+  z.total = z.k_codes + z.v_codes + z.k_out_idx + z.k_out_val + z.v_out_idx + z.v_out_val + z.v_scale +
+            z.k_scale + z.k_codebook + z.v_codebook + z.seq_len;
+  *out = z;
+  return KVQ_OK;
+}
+
+size_t kvq_workspace_bytes(const kvq_shape* s, int32_t max_len) {
+  if (check_shape(s) != KVQ_OK || max_len < 1) return 0;
+  return static_cast<size_t>(s->batch) * s->n_q_heads * n_chunks_for(max_len) * (kvq::kHeadDim + 2) * sizeof(float);
+}
+
+int kvq_quantize_append(const kvq_shape* s, const kvq_cache* c, const uint16_t* k_new, const uint16_t* v_new,
+                        int32_t n_max, const int32_t* n_new_host, const int32_t* seq_len_host,
+                        hipStream_t stream) {
+  int st = check_shape(s);
+  if (st != KVQ_OK) return st;
+  st = check_cache_common(s, c);
+  if (st != KVQ_OK) return st;
+  if (!c->k_codes || !c->v_codes || !c->v_scale || !c->k_scale || !c->k_codebook || !c->v_codebook)
+    return KVQ_ERR_INVALID;
+  if (!seq_len_host || n_max < 0) return KVQ_ERR_INVALID;
+  if (n_max > 0 && (!k_new || !v_new)) return KVQ_ERR_INVALID;
+  for (int b = 0; b < s->batch; ++b) {
+    const int32_t n = n_new_host ? n_new_host[b] : n_max;
+    if (n < 0 || n > n_max || seq_len_host[b] < 0) return KVQ_ERR_INVALID;
+    if (static_cast<int64_t>(seq_len_host[b]) + n > s->max_seq) return KVQ_ERR_CAPACITY;
+  }
+  const size_t H = s->n_kv_heads, S = s->max_seq, D = s->head_dim, k = s->n_outliers;
+  for (int b0 = 0; b0 < s->batch; b0 += kvq::kMaxBatchPerLaunch) {
+    const int nb = s->batch - b0 < kvq::kMaxBatchPerLaunch ? s->batch - b0 : kvq::kMaxBatchPerLaunch;
+    kvq::AppendArgs a;
+    std::memset(&a, 0, sizeof(a));
+    const size_t slot0 = static_cast<size_t>(b0) * H * S;
+    a.n_kv_heads = s->n_kv_heads;
+    a.max_seq = s->max_seq;
+    a.n_outliers = s->n_outliers;
+    a.n_max = n_max;
+    a.n_batch = nb;
+    a.k_new = k_new ? k_new + static_cast<size_t>(b0) * n_max * H * D : nullptr;
+    a.v_new = v_new ? v_new + static_cast<size_t>(b0) * n_max * H * D : nullptr;
+    a.k_codes = c->k_codes + slot0 * D * s->k_bits / 8;
+    a.v_codes = c->v_codes + slot0 * D * s->v_bits / 8;
+    a.k_idx = c->k_out_idx ? c->k_out_idx + slot0 * k : nullptr;
+    a.k_val = c->k_out_val ? c->k_out_val + slot0 * k : nullptr;
+    a.v_idx = c->v_out_idx ? c->v_out_idx + slot0 * k : nullptr;
+    a.v_val = c->v_out_val ? c->v_out_val + slot0 * k : nullptr;
+    a.v_scale = c->v_scale + slot0;
+    a.k_scale = c->k_scale;
+    a.k_cb = c->k_codebook;
+    a.v_cb = c->v_codebook;
+    a.seq_len = c->seq_len + b0;
+    for (int b = 0; b < nb; ++b) {
+      a.start[b] = seq_len_host[b0 + b];
+      a.count[b] = n_new_host ? n_new_host[b0 + b] : n_max;
+    }
+    hipError_t e = kvq::launch_append(s->k_bits, s->v_bits, a, stream);
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+  }
+  return KVQ_OK;
+}
+
+int kvq_qk_matvec(const kvq_shape* s, const kvq_cache* c, const void* q, int32_t q_is_fp16, float sm_scale,
+                  float* logits, int32_t max_len, hipStream_t stream) {
+  int st = check_shape(s);
+  if (st != KVQ_OK) return st;
+  st = check_cache_common(s, c);
+  if (st != KVQ_OK) return st;
+  if (!c->k_codes || !c->k_scale || !c->k_codebook || !q || !logits) return KVQ_ERR_INVALID;
+  if (q_is_fp16 != 0 && q_is_fp16 != 1) return KVQ_ERR_INVALID;
+  if (max_len < 1 || max_len > s->max_seq || !std::isfinite(sm_scale)) return KVQ_ERR_INVALID;
+  kvq::QkArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.n_q_heads = s->n_q_heads;
+  a.n_kv_heads = s->n_kv_heads;
+  a.max_seq = s->max_seq;
+  a.n_outliers = s->n_outliers;
+  a.max_len = max_len;
+  a.q_is_fp16 = q_is_fp16;
+  a.sm_scale = sm_scale;
+  a.theta_log2 = std::log2(static_cast<double>(s->rope_base)) * 2.0 / s->head_dim;
+  a.q = q;
+  a.k_codes = c->k_codes;
+  a.k_idx = c->k_out_idx;
+  a.k_val = c->k_out_val;
+  a.k_scale = c->k_scale;
+  a.k_cb = c->k_codebook;
+  a.seq_len = c->seq_len;
+  a.logits = logits;
+  return hip_status(kvq::launch_qk(s->k_bits, s->n_q_heads / s->n_kv_heads, s->batch, a, stream));
+}
+
+int kvq_pv_matvec(const kvq_shape* s, const kvq_cache* c, const float* logits, float* out, void* workspace,
+                  size_t workspace_bytes, int32_t max_len, hipStream_t stream) {
+  int st = check_shape(s);
+  if (st != KVQ_OK) return st;
+  st = check_cache_common(s, c);
+  if (st != KVQ_OK) return st;
+  if (!c->v_codes || !c->v_scale || !c->v_codebook || !logits || !out) return KVQ_ERR_INVALID;
+  if (max_len < 1 || max_len > s->max_seq) return KVQ_ERR_INVALID;
+  if (!workspace || workspace_bytes < kvq_workspace_bytes(s, max_len)) return KVQ_ERR_WORKSPACE;
+  kvq::PvArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.n_q_heads = s->n_q_heads;
+  a.n_kv_heads = s->n_kv_heads;
+  a.max_seq = s->max_seq;
+  a.n_outliers = s->n_outliers;
+  a.max_len = max_len;
+  a.n_chunks = static_cast<int32_t>(n_chunks_for(max_len));
+  a.logits = logits;
+  a.v_codes = c->v_codes;
+  a.v_idx = c->v_out_idx;
+  a.v_val = c->v_out_val;
+  a.v_scale = c->v_scale;
+  a.v_cb = c->v_codebook;
+  a.seq_len = c->seq_len;
+  a.partial = static_cast<float*>(workspace);
+  a.out = out;
+  return hip_status(kvq::launch_pv(s->v_bits, s->n_q_heads / s->n_kv_heads, s->batch, a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Kernel argument blocks and launchers shared between the kernels and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kMaxBatchPerLaunch = 128;  // per-sequence starts/counts travel in kernel args
+constexpr int kQkTokensPerBlock = 1024;  // 4 waves x 4 tiles of 64 tokens
+constexpr int kPvChunk = 1024;           // tokens per split of the softmax.V pass
+
+struct AppendArgs {
+  int32_t n_kv_heads, max_seq, n_outliers, n_max, n_batch;  // n_batch: sequences in this launch
+  const uint16_t* k_new;  // [n_batch][n_max][Hkv][D] (already offset to the first sequence)
+  const uint16_t* v_new;
+  uint8_t* k_codes;  // cache buffers offset to the first sequence of this launch
+  uint8_t* v_codes;
+  uint8_t* k_idx;
+  uint16_t* k_val;
+  uint8_t* v_idx;
+  uint16_t* v_val;
+  uint16_t* v_scale;
+  const float* k_scale;
+  const float* k_cb;
+  const float* v_cb;
+  int32_t* seq_len;  // offset to the first sequence of this launch
+  int32_t start[kMaxBatchPerLaunch];
+  int32_t count[kMaxBatchPerLaunch];
+};
+
+struct QkArgs {
+  int32_t n_q_heads, n_kv_heads, max_seq, n_outliers, max_len, q_is_fp16;
+  float sm_scale;
+  double theta_log2;  // log2(rope_base) * 2 / head_dim: theta_i = 2^(-i * theta_log2)
+  const void* q;
+  const uint8_t* k_codes;
+  const uint8_t* k_idx;
+  const uint16_t* k_val;
+  const float* k_scale;
+  const float* k_cb;
+  const int32_t* seq_len;
+  float* logits;
+};
+
+struct PvArgs {
+  int32_t n_q_heads, n_kv_heads, max_seq, n_outliers, max_len, n_chunks;
+  const float* logits;
+  const uint8_t* v_codes;
+  const uint8_t* v_idx;
+  const uint16_t* v_val;
+  const uint16_t* v_scale;
+  const float* v_cb;
+  const int32_t* seq_len;
+  float* partial;  // [B][Hq][n_chunks][D + 2]: o[D], m, l
+  float* out;      // [B][Hq][D]
+};
+
+hipError_t launch_append(int k_bits, int v_bits, const AppendArgs& a, hipStream_t s);
+hipError_t launch_qk(int k_bits, int group, int batch, const QkArgs& a, hipStream_t s);
+hipError_t launch_pv(int v_bits, int group, int batch, const PvArgs& a, hipStream_t s);
+
+}  // namespace kvq

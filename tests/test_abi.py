@@ -1,0 +1,94 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the header
+declares, sizes buffers as the documented layout says, and rejects bad arguments with
+the documented status codes before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_decode_kvq_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(kvq.LIB_PATH), reason="libkvq.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = kvq.load_library()
+    names = declared_functions()
+    assert set(names) == set(kvq.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.kvq_abi_version() == kvq.ABI_VERSION
+
+
+def cfg(**kw):
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, max_seq=256, k_bits=3, v_bits=4, n_outliers=2)
+    base.update(kw)
+    return kvq.CacheConfig(**base)
+
+
+def test_cache_sizes_match_layout():
+    c = cfg()
+    s = kvq.cache_sizes(c)
+    slots = 2 * 2 * 256
+    assert s.k_codes == slots * 128 * 3 // 8
+    assert s.v_codes == slots * 128 * 4 // 8
+    assert s.k_out_idx == slots * 2 and s.k_out_val == slots * 4
+    assert s.v_scale == slots * 2
+    assert s.k_scale == 2 * 128 * 4 and s.k_codebook == 8 * 4 and s.v_codebook == 16 * 4
+    assert s.total == sum(getattr(s, f) for f, _ in kvq.Sizes._fields_ if f != "total")
+
+
+def test_million_token_layer_footprint_fits():
+    """32 layers of a LLaMA-7B-shaped 2-bit cache with 1 % outliers at 1M tokens."""
+    c = cfg(batch=1, n_q_heads=32, n_kv_heads=32, max_seq=1 << 20, k_bits=2, v_bits=2, n_outliers=2)
+    per_layer = kvq.cache_sizes(c).total
+    fp16 = 2 * 32 * (1 << 20) * 128 * 2
+    assert 32 * per_layer < 288e9
+    assert fp16 / per_layer > 6.0
+
+
+def test_workspace_bytes():
+    c = cfg()
+    assert kvq.workspace_bytes(c, 1) == 2 * 8 * 1 * 130 * 4
+    assert kvq.workspace_bytes(c, 1025) == 2 * 8 * 2 * 130 * 4
+    assert kvq.workspace_bytes(c, 0) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, -2), ("k_bits", 5, -2), ("v_bits", 1, -2), ("n_q_heads", 6, -2),
+    ("max_seq", 100, -1), ("n_outliers", 129, -1), ("n_outliers", -1, -1), ("batch", 0, -1),
+    ("rope_base", 0.5, -1)])
+def test_bad_shapes_rejected(field, value, status):
+    c = cfg(**{field: value})
+    out = kvq.Sizes()
+    st = kvq.load_library().kvq_cache_sizes(ctypes.byref(c.shape()), ctypes.byref(out))
+    assert st == status
+
+
+def test_entry_points_reject_before_launch():
+    lib = kvq.load_library()
+    c = cfg()
+    shape = c.shape()
+    desc = kvq.CacheDesc()  # all NULL
+    lens = (ctypes.c_int32 * 2)(0, 0)
+    assert lib.kvq_quantize_append(ctypes.byref(shape), ctypes.byref(desc), None, None, 1, None, lens, None) == -1
+    assert lib.kvq_qk_matvec(ctypes.byref(shape), None, None, 0, 1.0, None, 10, None) == -1
+    # a descriptor with fake (never dereferenced) pointers: capacity and workspace checks
+    fake = kvq.CacheDesc(*([ctypes.c_void_p(4096)] * len(kvq.CacheDesc._fields_)))
+    big = (ctypes.c_int32 * 2)(250, 0)
+    assert lib.kvq_quantize_append(ctypes.byref(shape), ctypes.byref(fake), 4096, 4096, 10, None, big, None) == -3
+    assert lib.kvq_pv_matvec(ctypes.byref(shape), ctypes.byref(fake), 4096, 4096, 4096, 16, 10, None) == -4
+    assert lib.kvq_qk_matvec(ctypes.byref(shape), ctypes.byref(fake), 4096, 2, 1.0, 4096, 10, None) == -1
+    assert lib.kvq_qk_matvec(ctypes.byref(shape), ctypes.byref(fake), 4096, 0, 1.0, 4096, 257, None) == -1
+    for s in (0, -1, -2, -3, -4, -5, 7):
+        assert lib.kvq_status_string(s)
