@@ -34,6 +34,9 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-heads", type=int, default=24, help="kv-head streams the oracle times in the CPU leg")
+    p.add_argument("--kernel-steps", type=int, default=5, help="eager steps timed per kernel for the roofline")
+    p.add_argument("--no-graph", dest="graph", action="store_false",
+                   help="launch every kernel eagerly instead of replaying one HIP graph per step")
     return p.parse_args()
 
 
@@ -129,7 +132,7 @@ def main():
     dev = "cuda"
     kvq.load_library()
     L0 = wl.seq_len
-    total_new = (args.warmup + args.steps) * wl.n_new
+    total_new = (args.warmup + args.steps + args.kernel_steps) * wl.n_new
     max_seq = ((L0 + total_new + 63) // 64) * 64
     cfg = kvq.CacheConfig(wl.batch, wl.n_q_heads, wl.n_kv_heads, max_seq, wl.k_bits, wl.v_bits, wl.n_outliers,
                           wl.head_dim, wl.rope_base)
@@ -157,39 +160,73 @@ def main():
         torch.cuda.synchronize()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    kern_events = {"qk": [], "pv": []}
+    n_graph_steps = args.warmup + args.steps
 
-    def step(i, record):
+    def eager_step(i, kern_events=None):
         for lay in layers:
             c = lay["cache"]
             kvq.quantize_append(c, lay["new_k"][i], lay["new_v"][i])
             L = max(c.lengths)
-            if record:
+            if kern_events is not None:
                 e0, e1, e2 = ev(), ev(), ev()
                 e0.record()
             kvq.qk_matvec(c, lay["q"], lay["bufs"].logits, max_len=L)
-            if record:
+            if kern_events is not None:
                 e1.record()
             kvq.pv_matvec(c, lay["bufs"].logits, lay["bufs"].out, lay["bufs"].workspace, max_len=L)
-            if record:
+            if kern_events is not None:
                 e2.record()
                 kern_events["qk"].append((e0, e1))
                 kern_events["pv"].append((e1, e2))
 
+    # One HIP graph per decode step: every layer's device-positioned append of that
+    # step's new token, then q.K^T and softmax.V over the whole capacity bound (kernels
+    # read the live length from the device).
+    graphs = []
+    if args.graph:
+        for i in range(n_graph_steps):
+            g = torch.cuda.CUDAGraph()
+            saved = [list(l["cache"].lengths) for l in layers]
+            with torch.cuda.graph(g):
+                for lay in layers:
+                    c = lay["cache"]
+                    kvq.quantize_append(c, lay["new_k"][i], lay["new_v"][i], device_positions=True)
+                    kvq.qk_matvec(c, lay["q"], lay["bufs"].logits, max_len=max_seq)
+                    kvq.pv_matvec(c, lay["bufs"].logits, lay["bufs"].out, lay["bufs"].workspace, max_len=max_seq)
+            for l, sv in zip(layers, saved):
+                l["cache"].lengths = sv
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run_step(i):
+        if args.graph:
+            graphs[i].replay()
+            for l in layers:
+                l["cache"].lengths = [x + wl.n_new for x in l["cache"].lengths]
+        else:
+            eager_step(i)
+
     for i in range(args.warmup):
-        step(i, False)
+        run_step(i)
     torch.cuda.synchronize()
     start_len = max(layers[0]["cache"].lengths)
     t_start, t_end = ev(), ev()
     w0 = time.perf_counter()
     t_start.record()
     for i in range(args.steps):
-        step(args.warmup + i, True)
+        run_step(args.warmup + i)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_total = t_start.elapsed_time(t_end)
     ms_step = ms_total / args.steps
+    assert [int(x) for x in layers[0]["cache"].seq_len.cpu()] == layers[0]["cache"].lengths
+
+    # Per-kernel durations: eager steps with HIP events around each launch (same stream).
+    kern_events = {"qk": [], "pv": []}
+    for i in range(args.kernel_steps):
+        eager_step(n_graph_steps + i, kern_events)
+    torch.cuda.synchronize()
 
     # bytes: lengths grow by n_new per step; use the mean length over the timed steps
     L_mean = start_len + wl.n_new * (args.steps + 1) / 2.0
@@ -199,8 +236,10 @@ def main():
     kv_tok_s = args.layers * wl.batch * L_mean / (ms_step * 1e-3)
 
     kt = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in kern_events.items()}  # ms per launch
+    L_k = start_len + wl.n_new * (args.steps + (args.kernel_steps + 1) / 2.0)
+    qk_bk, pv_bk, _ = algorithmic_bytes(wl, L_k)
     dom = max(kt, key=kt.get)
-    dom_bytes = {"qk": qk_b, "pv": pv_b}[dom]
+    dom_bytes = {"qk": qk_bk, "pv": pv_bk}[dom]
     achieved = dom_bytes / (kt[dom] * 1e-3) / 1e9
     src = {"qk": ["qk.hip", "kvq_device.h"], "pv": ["pv.hip", "kvq_device.h"]}[dom]
     traffic = traffic_from_profile(dom, source_hash(src))
@@ -225,8 +264,9 @@ def main():
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "kv_tokens_per_s": round(kv_tok_s, 1),
         "kernel_ms": {k: round(v, 5) for k, v in kt.items()},
-        "kernel_gbs": {"qk": round(qk_b / (kt["qk"] * 1e-3) / 1e9, 1),
-                       "pv": round(pv_b / (kt["pv"] * 1e-3) / 1e9, 1)},
+        "kernel_gbs": {"qk": round(qk_bk / (kt["qk"] * 1e-3) / 1e9, 1),
+                       "pv": round(pv_bk / (kt["pv"] * 1e-3) / 1e9, 1)},
+        "graph": bool(args.graph),
         "wall_s_timed": round(wall, 3),
         "roofline": {"kernel": {"qk": "qk_kernel", "pv": "pv_partial_kernel+pv_combine_kernel"}[dom],
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -38,7 +38,8 @@
  *   v_scale   uint16 [B][H][S]     fp16 per-vector value scale (max |dense entry|)
  *   k_scale   float  [H][D]        frozen per-channel key scale (caller calibrated)
  *   k_codebook, v_codebook  float [2^bits], strictly ascending, in [-1, 1]
- *   seq_len   int32 [B]            tokens held per sequence (device copy)
+ *   seq_len   int32 [B]            tokens held per sequence (device copy; the length is
+ *                                  the low 24 bits, the high bits are zero between calls)
  * Bits of tokens at or beyond seq_len[b] are never read.  A cache whose buffers start
  * zero-filled holds zero bits there, which makes the packed buffers comparable byte for
  * byte.
@@ -69,7 +70,7 @@ typedef struct {
   int32_t n_q_heads;   /* Hq, a multiple of n_kv_heads; q head h reads kv head h / (Hq/Hkv) */
   int32_t n_kv_heads;  /* Hkv >= 1 */
   int32_t head_dim;    /* D, must be 128 */
-  int32_t max_seq;     /* S, cache capacity in tokens, a positive multiple of 64 */
+  int32_t max_seq;     /* S, cache capacity in tokens, a positive multiple of 64, < 2^24 */
   int32_t k_bits;      /* 2, 3 or 4 */
   int32_t v_bits;      /* 2, 3 or 4 */
   int32_t n_outliers;  /* k per (token, kv head) vector, 0 <= k <= D */
@@ -110,12 +111,19 @@ size_t kvq_workspace_bytes(const kvq_shape* shape, int32_t max_len);
  *   seq_len_host   host int32 [B]: current length of every sequence (must equal the
  *                  device seq_len).  Token j of sequence b goes to position
  *                  seq_len_host[b] + j.
+ *                  NULL selects device positions: each sequence's start is read from the
+ *                  device seq_len inside the kernel, so the call can be recorded once in a
+ *                  HIP graph and replayed every decode step.  The host cannot check
+ *                  capacity then: a sequence without room for its new tokens appends
+ *                  nothing and keeps its length (visible in seq_len).  Requires
+ *                  n_kv_heads <= 127.
  * Per new vector: the k largest |x| entries (ties to the lower channel) go to the outlier
  * store in ascending channel order with their fp16 bits; the dense rest (outlier slots
  * zeroed) is divided in float32 by the key's per-channel scale or by the value vector's
  * own max |dense| (0 -> all-zero u) and coded as the lowest j minimising |u - cb_j|.
- * Afterwards seq_len[b] = seq_len_host[b] + n_new (device), enqueued on `stream`.
- * Errors: KVQ_ERR_CAPACITY if any seq_len_host[b] + n_new > max_seq.
+ * Afterwards seq_len[b] = old length + n_new (device), enqueued on `stream`.
+ * Errors: KVQ_ERR_CAPACITY if any seq_len_host[b] + n_new > max_seq (host positions).
+ * Calls that overlap on one cache (e.g. on two streams) race.
  */
 int kvq_quantize_append(const kvq_shape* shape, const kvq_cache* cache, const uint16_t* k_new,
                         const uint16_t* v_new, int32_t n_max, const int32_t* n_new_host,

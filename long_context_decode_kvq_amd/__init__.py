@@ -183,8 +183,13 @@ class KVCache:
         return idx.view(shp), val.view(shp)
 
 
-def quantize_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, n_new=None, stream=None):
-    """kvq_quantize_append: k_new, v_new fp16 [B][n_max][Hkv][D] (keys pre-RoPE)."""
+def quantize_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, n_new=None, stream=None,
+                    device_positions: bool = False):
+    """kvq_quantize_append: k_new, v_new fp16 [B][n_max][Hkv][D] (keys pre-RoPE).
+
+    device_positions=True passes no host lengths: the kernel reads each sequence's
+    position from the device seq_len (graph-capturable).  The host mirror
+    ``cache.lengths`` is advanced for sequences that had room."""
     cfg = cache.cfg
     assert k_new.dtype == torch.float16 and v_new.dtype == torch.float16
     assert k_new.shape == v_new.shape and k_new.dim() == 4
@@ -192,13 +197,13 @@ def quantize_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, n_
     assert k_new.is_contiguous() and v_new.is_contiguous()
     n_max = k_new.shape[1]
     counts = [n_max] * cfg.batch if n_new is None else [int(x) for x in n_new]
-    starts = (ctypes.c_int32 * cfg.batch)(*cache.lengths)
+    starts = None if device_positions else (ctypes.c_int32 * cfg.batch)(*cache.lengths)
     cnt = (ctypes.c_int32 * cfg.batch)(*counts)
     st = load_library().kvq_quantize_append(ctypes.byref(cache._shape), ctypes.byref(cache._desc),
                                             k_new.data_ptr(), v_new.data_ptr(), n_max, cnt, starts,
                                             _stream(stream))
     _check("kvq_quantize_append", st)
-    cache.lengths = [a + b for a, b in zip(cache.lengths, counts)]
+    cache.lengths = [a + b if a + b <= cfg.max_seq else a for a, b in zip(cache.lengths, counts)]
 
 
 def qk_matvec(cache: KVCache, q: torch.Tensor, logits: torch.Tensor, sm_scale: float | None = None,

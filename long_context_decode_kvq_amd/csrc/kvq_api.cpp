@@ -18,7 +18,7 @@ bool group_ok(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 int check_shape(const kvq_shape* s) {
   if (!s) return KVQ_ERR_INVALID;
   if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->max_seq < 1) return KVQ_ERR_INVALID;
-  if (s->max_seq % kvq::kTile != 0) return KVQ_ERR_INVALID;
+  if (s->max_seq % kvq::kTile != 0 || s->max_seq > kvq::kMaxSeqLimit) return KVQ_ERR_INVALID;
   if (s->n_q_heads % s->n_kv_heads != 0) return KVQ_ERR_INVALID;
   if (s->n_outliers < 0) return KVQ_ERR_INVALID;
   if (!(s->rope_base > 1.0f) || !std::isfinite(s->rope_base)) return KVQ_ERR_INVALID;
@@ -100,12 +100,17 @@ int kvq_quantize_append(const kvq_shape* s, const kvq_cache* c, const uint16_t* 
   if (st != KVQ_OK) return st;
   if (!c->k_codes || !c->v_codes || !c->v_scale || !c->k_scale || !c->k_codebook || !c->v_codebook)
     return KVQ_ERR_INVALID;
-  if (!seq_len_host || n_max < 0) return KVQ_ERR_INVALID;
+  if (n_max < 0) return KVQ_ERR_INVALID;
   if (n_max > 0 && (!k_new || !v_new)) return KVQ_ERR_INVALID;
+  const bool device_positions = seq_len_host == nullptr;
+  if (device_positions && s->n_kv_heads > kvq::kMaxKvHeadsDevicePos) return KVQ_ERR_UNSUPPORTED;
   for (int b = 0; b < s->batch; ++b) {
     const int32_t n = n_new_host ? n_new_host[b] : n_max;
-    if (n < 0 || n > n_max || seq_len_host[b] < 0) return KVQ_ERR_INVALID;
-    if (static_cast<int64_t>(seq_len_host[b]) + n > s->max_seq) return KVQ_ERR_CAPACITY;
+    if (n < 0 || n > n_max) return KVQ_ERR_INVALID;
+    if (!device_positions) {
+      if (seq_len_host[b] < 0) return KVQ_ERR_INVALID;
+      if (static_cast<int64_t>(seq_len_host[b]) + n > s->max_seq) return KVQ_ERR_CAPACITY;
+    }
   }
   const size_t H = s->n_kv_heads, S = s->max_seq, D = s->head_dim, k = s->n_outliers;
   for (int b0 = 0; b0 < s->batch; b0 += kvq::kMaxBatchPerLaunch) {
@@ -118,6 +123,7 @@ int kvq_quantize_append(const kvq_shape* s, const kvq_cache* c, const uint16_t* 
     a.n_outliers = s->n_outliers;
     a.n_max = n_max;
     a.n_batch = nb;
+    a.device_positions = device_positions ? 1 : 0;
     a.k_new = k_new ? k_new + static_cast<size_t>(b0) * n_max * H * D : nullptr;
     a.v_new = v_new ? v_new + static_cast<size_t>(b0) * n_max * H * D : nullptr;
     a.k_codes = c->k_codes + slot0 * D * s->k_bits / 8;
@@ -132,7 +138,7 @@ int kvq_quantize_append(const kvq_shape* s, const kvq_cache* c, const uint16_t* 
     a.v_cb = c->v_codebook;
     a.seq_len = c->seq_len + b0;
     for (int b = 0; b < nb; ++b) {
-      a.start[b] = seq_len_host[b0 + b];
+      a.start[b] = device_positions ? 0 : seq_len_host[b0 + b];
       a.count[b] = n_new_host ? n_new_host[b0 + b] : n_max;
     }
     hipError_t e = kvq::launch_append(s->k_bits, s->v_bits, a, stream);

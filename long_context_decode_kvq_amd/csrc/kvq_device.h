@@ -10,6 +10,9 @@ constexpr int kHeadDim = 128;
 constexpr int kHalf = kHeadDim / 2;  // rotary pairs per vector
 constexpr int kTile = 64;            // tokens per value tile and per QK wave pass
 constexpr int kWave = 64;
+// seq_len words hold the length in their low 24 bits; the high bits are an arrival
+// counter used only while a device-positioned append is in flight.
+constexpr int32_t kLenMask = 0x00ffffff;
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
@@ -76,6 +79,22 @@ __device__ __forceinline__ uint32_t nearest_code(float u, const float* cb) {
     }
   }
   return best;
+}
+
+// Index of the codebook entry nearest to 0 (the code of every dense-zero entry, in
+// particular of every outlier slot): smallest j minimising |0 - cb[j]|.
+template <int NC>
+__device__ __forceinline__ int zero_code_index(const float* cb) {
+  int j0 = 0;
+  float bd = fabsf(0.0f - cb[0]);
+  for (int j = 1; j < NC; ++j) {
+    const float d = fabsf(0.0f - cb[j]);
+    if (d < bd) {
+      bd = d;
+      j0 = j;
+    }
+  }
+  return j0;
 }
 
 // cos/sin of 2*pi*r for a revolution count r already reduced to [0, 1).

@@ -9,9 +9,12 @@ namespace kvq {
 constexpr int kMaxBatchPerLaunch = 128;  // per-sequence starts/counts travel in kernel args
 constexpr int kQkTokensPerBlock = 1024;  // 4 waves x 4 tiles of 64 tokens
 constexpr int kPvChunk = 1024;           // tokens per split of the softmax.V pass
+constexpr int kMaxSeqLimit = (1 << 24) - 64;  // lengths live in the low 24 bits of seq_len
+constexpr int kMaxKvHeadsDevicePos = 127;     // arrival counter width of a device-positioned append
 
 struct AppendArgs {
   int32_t n_kv_heads, max_seq, n_outliers, n_max, n_batch;  // n_batch: sequences in this launch
+  int32_t device_positions;  // 1: start positions come from seq_len on the device
   const uint16_t* k_new;  // [n_batch][n_max][Hkv][D] (already offset to the first sequence)
   const uint16_t* v_new;
   uint8_t* k_codes;  // cache buffers offset to the first sequence of this launch
@@ -25,12 +28,13 @@ struct AppendArgs {
   const float* k_cb;
   const float* v_cb;
   int32_t* seq_len;  // offset to the first sequence of this launch
-  int32_t start[kMaxBatchPerLaunch];
+  int32_t start[kMaxBatchPerLaunch];  // host positions (unused with device_positions)
   int32_t count[kMaxBatchPerLaunch];
 };
 
 struct QkArgs {
   int32_t n_q_heads, n_kv_heads, max_seq, n_outliers, max_len, q_is_fp16;
+  int32_t tiles_per_wave;  // set by the launcher
   float sm_scale;
   double theta_log2;  // log2(rope_base) * 2 / head_dim: theta_i = 2^(-i * theta_log2)
   const void* q;

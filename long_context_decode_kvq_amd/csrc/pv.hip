@@ -6,12 +6,13 @@
 // outliers are added back.  The split over the sequence lets a single long sequence fill
 // the GPU.
 //
-// pv_partial: one block per (sequence, kv head, chunk of 1024 tokens).  Pass 1 reads the
-// chunk's logits (one thread per token) for every query head of the group, forms
-// p_t = exp(l_t - m) and the per-token weight w_t = p_t * s_t, and scatters the outlier
-// corrections p_t * (x_c - zc * s_t) into LDS.  Pass 2 walks the channel-major value
-// tiles with one lane per channel pair, so each lane accumulates its two channels over
-// the tile's 64 tokens in registers.  The chunk's (o, m, l) go to the workspace.
+// pv_partial: one block per (sequence, kv head, chunk of 1024 tokens).  Every wave first
+// issues the loads of its four value tiles, so they are in flight during pass 1, which
+// reads the chunk's logits (one thread per token) for every query head of the group,
+// forms p_t = exp(l_t - m) and the per-token weight w_t = p_t * s_t, and scatters the
+// outlier corrections p_t * (x_c - zc * s_t) into LDS.  Pass 2 walks the channel-major
+// tiles with one lane per channel pair: the 2b-bit field holding two consecutive tokens
+// of one channel indexes a table of (cb[a], cb[b]), so one lookup decodes two tokens.
 // pv_combine: one block per (sequence, query head) merges the chunks.
 #include <type_traits>
 
@@ -25,15 +26,17 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kTokPerThread = kPvChunk / kThreads;
 constexpr int kTilesPerChunk = kPvChunk / kTile;
+constexpr int kTilesPerWave = kTilesPerChunk / kWaves;
 
 template <int VB, int G>
 __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   constexpr int kNc = 1 << VB;
   constexpr int kLaneWords = 4 * VB;
   constexpr int kChanBits = 64 * VB;
+  constexpr int kPairEntries = 1 << (2 * VB);
 
-  __shared__ float cb[kNc];
-  __shared__ float wt[G][kPvChunk];          // p_t * s_t
+  __shared__ float2 lut2[kPairEntries];      // (cb[a], cb[b]) for a token pair
+  __shared__ float2 wt[G][kPvChunk / 2];     // (w_t, w_{t+1}), w = p * s
   __shared__ float osp[G][kHeadDim];         // outlier corrections
   __shared__ float part[kWaves][G][kHeadDim];
   __shared__ float red[kWaves][G];
@@ -48,10 +51,11 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   const int H = a.n_kv_heads;
   const int S = a.max_seq;
   const int k = a.n_outliers;
-  const int L = min(a.seq_len[seq], a.max_len);
+  const int L = min(a.seq_len[seq] & kLenMask, a.max_len);
   const int c0 = chunk * kPvChunk;
   const int n = min(L - c0, kPvChunk);
   const size_t part_stride = kHeadDim + 2;
+  const size_t stream = static_cast<size_t>(seq) * H + kvh;
 
   if (n <= 0) {
     for (int e = tid; e < G * (kHeadDim + 2); e += kThreads) {
@@ -62,22 +66,29 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
     return;
   }
 
-  if (tid < kNc) cb[tid] = a.v_cb[tid];
-  for (int e = tid; e < G * kHeadDim; e += kThreads) (&osp[0][0])[e] = 0.0f;
-  if (tid == 0) {
-    int j0 = 0;
-    float bd = fabsf(0.0f - a.v_cb[0]);
-    for (int j = 1; j < kNc; ++j) {
-      const float d = fabsf(0.0f - a.v_cb[j]);
-      if (d < bd) {
-        bd = d;
-        j0 = j;
+  // ---- issue this wave's value-tile loads first -------------------------------------
+  const int wave_tile0 = wave * kTilesPerWave;  // tile index inside the chunk
+  uint32_t w[kTilesPerWave][kLaneWords];
+  const uint8_t* tiles = a.v_codes + (stream * (S / kTile) + c0 / kTile) * (1024 * VB);
+#pragma unroll
+  for (int tl = 0; tl < kTilesPerWave; ++tl) {
+    if ((wave_tile0 + tl) * kTile < n) {
+      const uint4* p = reinterpret_cast<const uint4*>(tiles + static_cast<size_t>(wave_tile0 + tl) * (1024 * VB) +
+                                                      lane * (16 * VB));
+#pragma unroll
+      for (int v = 0; v < VB; ++v) {
+        const uint4 d = p[v];
+        w[tl][4 * v + 0] = d.x;
+        w[tl][4 * v + 1] = d.y;
+        w[tl][4 * v + 2] = d.z;
+        w[tl][4 * v + 3] = d.w;
       }
     }
-    zc = a.v_cb[j0];
   }
 
-  const size_t stream = static_cast<size_t>(seq) * H + kvh;
+  for (int e = tid; e < kPairEntries; e += kThreads) lut2[e] = make_float2(a.v_cb[e & (kNc - 1)], a.v_cb[e >> VB]);
+  for (int e = tid; e < G * kHeadDim; e += kThreads) (&osp[0][0])[e] = 0.0f;
+  if (tid == 0) zc = a.v_cb[zero_code_index<kNc>(a.v_cb)];
 
   // ---- pass 1: max, exp, weights, outlier scatter ----------------------------------
   float lg[G][kTokPerThread];
@@ -101,7 +112,7 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   for (int h = 0; h < G; ++h) {
     m[h] = red[0][h];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) m[h] = fmaxf(m[h], red[w][h]);
+    for (int ww = 1; ww < kWaves; ++ww) m[h] = fmaxf(m[h], red[ww][h]);
   }
   __syncthreads();
 
@@ -119,7 +130,7 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
     for (int h = 0; h < G; ++h) {
       p[h] = valid ? expf(lg[h][u] - m[h]) : 0.0f;
       lsum[h] += p[h];
-      wt[h][t] = p[h] * s;
+      reinterpret_cast<float*>(&wt[h][0])[t] = p[h] * s;
     }
     if (valid) {
       for (int j = 0; j < k; ++j) {
@@ -141,31 +152,22 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   float acc[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) acc[h][0] = acc[h][1] = 0.0f;
-  const uint8_t* tiles = a.v_codes + (stream * (S / kTile) + c0 / kTile) * (1024 * VB);
-  for (int tl = wave; tl < kTilesPerChunk; tl += kWaves) {
-    if (tl * kTile >= n) break;
-    uint32_t w[kLaneWords];
-    const uint4* p = reinterpret_cast<const uint4*>(tiles + static_cast<size_t>(tl) * (1024 * VB) + lane * (16 * VB));
 #pragma unroll
-    for (int v = 0; v < VB; ++v) {
-      const uint4 d = p[v];
-      w[4 * v + 0] = d.x;
-      w[4 * v + 1] = d.y;
-      w[4 * v + 2] = d.z;
-      w[4 * v + 3] = d.w;
+  for (int tl = 0; tl < kTilesPerWave; ++tl) {
+    if ((wave_tile0 + tl) * kTile < n) {
+      const float2* wrow = &wt[0][(wave_tile0 + tl) * (kTile / 2)];
+      static_for<0, kTile / 2>([&](auto mc) {
+        constexpr int mm = decltype(mc)::value;
+        const float2 v0 = lut2[field<2 * VB, 2 * VB * mm>(w[tl])];
+        const float2 v1 = lut2[field<2 * VB, kChanBits + 2 * VB * mm>(w[tl])];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float2 ww = wrow[h * (kPvChunk / 2) + mm];
+          acc[h][0] = fmaf(ww.y, v0.y, fmaf(ww.x, v0.x, acc[h][0]));
+          acc[h][1] = fmaf(ww.y, v1.y, fmaf(ww.x, v1.x, acc[h][1]));
+        }
+      });
     }
-    const float* wrow = &wt[0][tl * kTile];
-    static_for<0, kTile>([&](auto tc) {
-      constexpr int tau = decltype(tc)::value;
-      const float v0 = cb[field<VB, tau * VB>(w)];
-      const float v1 = cb[field<VB, kChanBits + tau * VB>(w)];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float ww = wrow[h * kPvChunk + tau];
-        acc[h][0] += ww * v0;
-        acc[h][1] += ww * v1;
-      }
-    });
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -178,39 +180,62 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
     const int h = e / kHeadDim, c = e % kHeadDim;
     float o = osp[h][c];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) o += part[w][h][c];
+    for (int ww = 0; ww < kWaves; ++ww) o += part[ww][h][c];
     float* dst = a.partial + ((static_cast<size_t>(seq) * a.n_q_heads + kvh * G + h) * a.n_chunks + chunk) * part_stride;
     dst[c] = o;
     if (c == 0) {
       float l = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) l += red[w][h];
+      for (int ww = 0; ww < kWaves; ++ww) l += red[ww][h];
       dst[kHeadDim] = m[h];
       dst[kHeadDim + 1] = l;
     }
   }
 }
 
-__global__ __launch_bounds__(128) void pv_combine_kernel(PvArgs a) {
-  const int c = threadIdx.x;
+// One block per (sequence, query head): 256 threads = 128 channels x 2 halves of the
+// chunk list.  Loads are independent, so the chunk loop keeps several in flight.
+__global__ __launch_bounds__(256) void pv_combine_kernel(PvArgs a) {
+  __shared__ float red[4];
+  __shared__ float acc_n[kHeadDim], acc_d[kHeadDim];
+  const int tid = threadIdx.x;
+  const int c = tid & (kHeadDim - 1);
+  const int half = tid >> 7;
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const size_t part_stride = kHeadDim + 2;
   const float* src = a.partial + (static_cast<size_t>(seq) * a.n_q_heads + h) * a.n_chunks * part_stride;
-  const int L = min(a.seq_len[seq], a.max_len);
+  const int L = min(a.seq_len[seq] & kLenMask, a.max_len);
   const int nc = (L + kPvChunk - 1) / kPvChunk;
+
   float M = -INFINITY;
-  for (int j = 0; j < nc; ++j) M = fmaxf(M, src[j * part_stride + kHeadDim]);
+  for (int j = tid; j < nc; j += 256) M = fmaxf(M, src[j * part_stride + kHeadDim]);
+  M = wave_max_f32(M);
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
   float num = 0.0f, den = 0.0f;
   if (M > -INFINITY) {
-    for (int j = 0; j < nc; ++j) {
-      const float mj = src[j * part_stride + kHeadDim];
+#pragma unroll 4
+    for (int j = half; j < nc; j += 2) {
+      const float* pj = src + j * part_stride;
+      const float mj = pj[kHeadDim];
       const float wj = mj > -INFINITY ? expf(mj - M) : 0.0f;
-      num += wj * src[j * part_stride + c];
-      den += wj * src[j * part_stride + kHeadDim + 1];
+      num += wj * pj[c];
+      den += wj * pj[kHeadDim + 1];
     }
   }
-  a.out[(static_cast<size_t>(seq) * a.n_q_heads + h) * kHeadDim + c] = den > 0.0f ? num / den : 0.0f;
+  if (half == 1) {
+    acc_n[c] = num;
+    acc_d[c] = den;
+  }
+  __syncthreads();
+  if (half == 0) {
+    num += acc_n[c];
+    den += acc_d[c];
+    a.out[(static_cast<size_t>(seq) * a.n_q_heads + h) * kHeadDim + c] = den > 0.0f ? num / den : 0.0f;
+  }
 }
 
 template <int VB, int G>
@@ -219,7 +244,7 @@ hipError_t launch_pv_t(int batch, const PvArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((pv_partial_kernel<VB, G>), grid, dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pv_combine_kernel, dim3(a.n_q_heads, batch), dim3(kHeadDim), 0, s, a);
+  hipLaunchKernelGGL(pv_combine_kernel, dim3(a.n_q_heads, batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

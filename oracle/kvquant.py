@@ -11,9 +11,9 @@ Sources (the KVQuant pages):
        datatypes, (iv) per-vector dense-and-sparse quantization that isolates outliers
        separately for each vector; decode is memory- and bandwidth-bound.
   [P2] "KVQuant" paper note (phantomic12 inference-research), "Four components"
-       paragraph: keys quantized per channel and *before* the rotary embedding so the
-       per-position rotation cannot smear values across buckets; a codebook per layer;
-       outliers isolated per vector rather than globally.
+       paragraph: keys quantized per channel and before the rotary embedding (the
+       position-dependent rotation would otherwise mix values between quantization
+       levels); a codebook per layer; outliers isolated per vector, not globally.
 
 The pages give the components in prose only; every step below that they leave open is
 a stated reading (see the notes on each function).  Precision: the quantization

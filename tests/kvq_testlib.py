@@ -71,27 +71,29 @@ class Case:
         return oracle.decode_head(self.q_head(b, hq), c, self.ks[h], self.cbk, self.cbv, self.wl.rope_base, sm)
 
     # ------------------------------------------------------------------- GPU side --
-    def build_gpu(self, chunks=None):
+    def build_gpu(self, chunks=None, upto=None):
         """Fill a KVCache through kvq_quantize_append.  ``chunks``: list of per-call token
-        counts (same for every sequence, clipped to its length); default one bulk call."""
+        counts (same for every sequence, clipped to its length); default one bulk call.
+        ``upto``: per-sequence lengths to stop at (default: the case's lengths)."""
         import long_context_decode_kvq_amd as kvq
         wl = self.wl
         cfg = kvq.CacheConfig(wl.batch, wl.n_q_heads, wl.n_kv_heads, self.max_seq, wl.k_bits, wl.v_bits,
                               self.k, D, wl.rope_base)
         cache = kvq.KVCache(cfg, torch.from_numpy(self.ks), torch.from_numpy(self.cbk),
                             torch.from_numpy(self.cbv), device=self.device)
-        total = int(self.lens.max())
+        target = self.lens if upto is None else np.asarray(upto, dtype=np.int64)
+        total = int(target.max())
         chunks = chunks or [total]
         pos = np.zeros(wl.batch, dtype=np.int64)
         for n in chunks:
-            hi = np.minimum(pos + n, self.lens)
+            hi = np.minimum(pos + n, target)
             cnt = hi - pos
             if cnt.max() <= 0:
                 continue
             k_new, v_new = stack_new(wl, self.streams, pos, hi, int(cnt.max()), self.device)
             kvq.quantize_append(cache, k_new, v_new, n_new=cnt.tolist())
             pos = hi
-        assert np.array_equal(pos, self.lens)
+        assert np.array_equal(pos, target)
         return cache
 
     # ------------------------------------------------------------ expected buffers --
