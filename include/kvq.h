@@ -37,7 +37,8 @@
  *   v_out_idx, v_out_val           the same for values
  *   v_scale   uint16 [B][H][S]     fp16 per-vector value scale (max |dense entry|)
  *   k_scale   float  [H][D]        frozen per-channel key scale (caller calibrated)
- *   k_codebook, v_codebook  float [2^bits], strictly ascending, in [-1, 1]
+ *   k_codebook, v_codebook  fp16 [2^bits] (uint16_t bits), strictly ascending, in [-1, 1];
+ *             the quantizer compares against their exact float32 values
  *   seq_len   int32 [B]            tokens held per sequence (device copy; the length is
  *                                  the low 24 bits, the high bits are zero between calls)
  * Bits of tokens at or beyond seq_len[b] are never read.  A cache whose buffers start
@@ -85,7 +86,7 @@ typedef struct {
   uint16_t *v_out_val;
   uint16_t *v_scale;
   const float *k_scale;
-  const float *k_codebook, *v_codebook;
+  const uint16_t *k_codebook, *v_codebook;
   int32_t *seq_len;
 } kvq_cache;
 

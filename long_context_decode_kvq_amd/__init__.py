@@ -130,6 +130,15 @@ def workspace_bytes(cfg: CacheConfig, max_len: int) -> int:
     return int(load_library().kvq_workspace_bytes(ctypes.byref(cfg.shape()), int(max_len)))
 
 
+def _fp16_codebook(cb: torch.Tensor, device) -> torch.Tensor:
+    """The codebook as fp16 bits (int16 storage); its values must be fp16 numbers."""
+    c = cb.detach().to("cpu")
+    h = c.to(torch.float16)
+    if not torch.equal(h.to(c.dtype), c):
+        raise ValueError("codebook entries must be exactly representable in fp16")
+    return h.view(torch.int16).to(device).contiguous()
+
+
 class KVCache:
     """Device buffers of one layer's compressed KV cache, laid out as ``include/kvq.h``
     documents; all zero-filled at creation."""
@@ -150,8 +159,8 @@ class KVCache:
         self.v_out_val = torch.zeros(n_slots * k, **i16)
         self.v_scale = torch.zeros(n_slots, **i16)
         self.k_scale = k_scale.to(device=device, dtype=torch.float32).contiguous()
-        self.k_codebook = k_codebook.to(device=device, dtype=torch.float32).contiguous()
-        self.v_codebook = v_codebook.to(device=device, dtype=torch.float32).contiguous()
+        self.k_codebook = _fp16_codebook(k_codebook, device)
+        self.v_codebook = _fp16_codebook(v_codebook, device)
         assert self.k_scale.numel() == cfg.n_kv_heads * cfg.head_dim
         assert self.k_codebook.numel() == 1 << cfg.k_bits and self.v_codebook.numel() == 1 << cfg.v_bits
         self.seq_len = torch.zeros(cfg.batch, dtype=torch.int32, device=device)

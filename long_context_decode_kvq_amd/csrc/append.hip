@@ -88,8 +88,8 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
       if (blockIdx.x == 0 && kvh == 0) a.seq_len[seq] = a.start[seq] + count;
     }
   }
-  if (tid < kNcK) cbk[tid] = a.k_cb[tid];
-  if (tid < kNcV) cbv[tid] = a.v_cb[tid];
+  if (tid < kNcK) cbk[tid] = half_bits_to_float(a.k_cb[tid]);
+  if (tid < kNcV) cbv[tid] = half_bits_to_float(a.v_cb[tid]);
   __syncthreads();
   const int start = s_start;
   if (start < 0 || count <= 0) return;

@@ -44,6 +44,22 @@ size_t n_chunks_for(int32_t max_len) { return (static_cast<size_t>(max_len) + kv
 
 }  // namespace
 
+namespace kvq {
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+}  // namespace kvq
+
 extern "C" {
 
 int kvq_abi_version(void) { return KVQ_ABI_VERSION; }
@@ -77,8 +93,8 @@ int kvq_cache_sizes(const kvq_shape* s, kvq_sizes* out) {
   z.v_out_val = slots * s->n_outliers * 2;
   z.v_scale = slots * 2;
   z.k_scale = static_cast<size_t>(s->n_kv_heads) * D * 4;
-  z.k_codebook = (static_cast<size_t>(1) << s->k_bits) * 4;
-  z.v_codebook = (static_cast<size_t>(1) << s->v_bits) * 4;
+  z.k_codebook = (static_cast<size_t>(1) << s->k_bits) * 2;
+  z.v_codebook = (static_cast<size_t>(1) << s->v_bits) * 2;
   z.seq_len = static_cast<size_t>(s->batch) * 4;
   z.total = z.k_codes + z.v_codes + z.k_out_idx + z.k_out_val + z.v_out_idx + z.v_out_val + z.v_scale +
             z.k_scale + z.k_codebook + z.v_codebook + z.seq_len;
@@ -193,7 +209,6 @@ int kvq_pv_matvec(const kvq_shape* s, const kvq_cache* c, const float* logits, f
   a.max_seq = s->max_seq;
   a.n_outliers = s->n_outliers;
   a.max_len = max_len;
-  a.n_chunks = static_cast<int32_t>(n_chunks_for(max_len));
   a.logits = logits;
   a.v_codes = c->v_codes;
   a.v_idx = c->v_out_idx;

@@ -25,8 +25,8 @@ struct AppendArgs {
   uint16_t* v_val;
   uint16_t* v_scale;
   const float* k_scale;
-  const float* k_cb;
-  const float* v_cb;
+  const uint16_t* k_cb;  // fp16 codebooks
+  const uint16_t* v_cb;
   int32_t* seq_len;  // offset to the first sequence of this launch
   int32_t start[kMaxBatchPerLaunch];  // host positions (unused with device_positions)
   int32_t count[kMaxBatchPerLaunch];
@@ -42,23 +42,35 @@ struct QkArgs {
   const uint8_t* k_idx;
   const uint16_t* k_val;
   const float* k_scale;
-  const float* k_cb;
+  const uint16_t* k_cb;  // fp16 codebook
   const int32_t* seq_len;
   float* logits;
 };
 
 struct PvArgs {
-  int32_t n_q_heads, n_kv_heads, max_seq, n_outliers, max_len, n_chunks;
+  int32_t n_q_heads, n_kv_heads, max_seq, n_outliers, max_len;
+  int32_t tiles_per_block, n_parts;  // set by the launcher: split of each stream into parts
   const float* logits;
   const uint8_t* v_codes;
   const uint8_t* v_idx;
   const uint16_t* v_val;
   const uint16_t* v_scale;
-  const float* v_cb;
+  const uint16_t* v_cb;  // fp16 codebook
   const int32_t* seq_len;
-  float* partial;  // [B][Hq][n_chunks][D + 2]: o[D], m, l
+  float* partial;  // [B][Hq][n_parts][D + 2]: o[D], m, l
   float* out;      // [B][Hq][D]
 };
+
+// Compute units of the current device (queried once per device, then cached).
+int device_cu_count();
+
+// Resident blocks of `kernel` per CU at `threads` per block (queried once, then cached by
+// the caller), at least 1.
+inline int blocks_per_cu(const void* kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) n = 1;
+  return n;
+}
 
 hipError_t launch_append(int k_bits, int v_bits, const AppendArgs& a, hipStream_t s);
 hipError_t launch_qk(int k_bits, int group, int batch, const QkArgs& a, hipStream_t s);

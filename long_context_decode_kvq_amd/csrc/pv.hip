@@ -6,14 +6,19 @@
 // outliers are added back.  The split over the sequence lets a single long sequence fill
 // the GPU.
 //
-// pv_partial: one block per (sequence, kv head, chunk of 1024 tokens).  Every wave first
-// issues the loads of its four value tiles, so they are in flight during pass 1, which
-// reads the chunk's logits (one thread per token) for every query head of the group,
-// forms p_t = exp(l_t - m) and the per-token weight w_t = p_t * s_t, and scatters the
-// outlier corrections p_t * (x_c - zc * s_t) into LDS.  Pass 2 walks the channel-major
-// tiles with one lane per channel pair: the 2b-bit field holding two consecutive tokens
-// of one channel indexes a table of (cb[a], cb[b]), so one lookup decodes two tokens.
-// pv_combine: one block per (sequence, query head) merges the chunks.
+// pv_partial: the device's block slots are shared equally among the (sequence, kv head)
+// streams; a block owns a contiguous run of 64-token tiles of one stream and each of its
+// four waves walks its own share of that run independently, with its own running
+// (max, sum) softmax state and the next tile's data already in flight.  Per tile:
+//   * lane = token: the wave's max logit per query head rescales the running state,
+//     p_t = exp(l_t - m), w_t = p_t * s_t, and the outlier corrections
+//     p_t * (x_c - zc * s_t) are added into the wave's own LDS row of channels;
+//   * lane = channel pair (2l, 2l+1): the 2b-bit field holding two consecutive tokens of
+//     one channel indexes a small table of fp16 pairs (cb[a], cb[b]); w_t reaches every
+//     lane as a scalar operand (read from lane t) of a mixed-precision FMA.
+// The four waves merge their states once at the end; each block writes one (o, m, l).
+// pv_combine: one block per (sequence, query head) merges the block partials.
+#include <algorithm>
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -24,177 +29,214 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kTokPerThread = kPvChunk / kThreads;
-constexpr int kTilesPerChunk = kPvChunk / kTile;
-constexpr int kTilesPerWave = kTilesPerChunk / kWaves;
+constexpr int kMinTilesPerBlock = 16;   // parts never outnumber ceil(max_len / 1024)
+constexpr int kPrefetchOutliers = 2;    // outliers per token held in registers
+
+template <int VB, int G>
+struct TileData {
+  uint32_t w[4 * VB];  // this lane's value-tile words (channels 2l, 2l+1)
+  float lg[G];         // logit of token `lane` for every query head of the group
+  uint32_t sv;         // fp16 value scale of token `lane`
+  uint32_t oi, ov;     // its first two outliers: channels (u8 x2) and fp16 values
+};
 
 template <int VB, int G>
 __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   constexpr int kNc = 1 << VB;
-  constexpr int kLaneWords = 4 * VB;
   constexpr int kChanBits = 64 * VB;
   constexpr int kPairEntries = 1 << (2 * VB);
 
-  __shared__ float2 lut2[kPairEntries];      // (cb[a], cb[b]) for a token pair
-  __shared__ float2 wt[G][kPvChunk / 2];     // (w_t, w_{t+1}), w = p * s
-  __shared__ float osp[G][kHeadDim];         // outlier corrections
-  __shared__ float part[kWaves][G][kHeadDim];
-  __shared__ float red[kWaves][G];
+  __shared__ uint32_t lut2[kPairEntries];         // fp16 (cb[a], cb[b]) for a token pair
+  __shared__ float cbs[kNc];
+  __shared__ float osp[kWaves][G][kHeadDim];      // per-wave outlier corrections
+  __shared__ float wm[kWaves][G], wl[kWaves][G];  // per-wave max and sum
+  __shared__ float wo[kWaves][G][kHeadDim];       // per-wave weighted sums
   __shared__ float zc;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int chunk = blockIdx.x;
   const int kvh = blockIdx.y;
   const int seq = blockIdx.z;
   const int H = a.n_kv_heads;
   const int S = a.max_seq;
   const int k = a.n_outliers;
   const int L = min(a.seq_len[seq] & kLenMask, a.max_len);
-  const int c0 = chunk * kPvChunk;
-  const int n = min(L - c0, kPvChunk);
+  const int n_tiles = (L + kTile - 1) / kTile;
+  const int tile_lo = blockIdx.x * a.tiles_per_block;
+  const int tile_hi = min(tile_lo + a.tiles_per_block, n_tiles);
   const size_t part_stride = kHeadDim + 2;
   const size_t stream = static_cast<size_t>(seq) * H + kvh;
+  auto part_ptr = [&](int h) {
+    return a.partial + ((static_cast<size_t>(seq) * a.n_q_heads + kvh * G + h) * a.n_parts + blockIdx.x) * part_stride;
+  };
 
-  if (n <= 0) {
+  if (tile_lo >= tile_hi) {
     for (int e = tid; e < G * (kHeadDim + 2); e += kThreads) {
       const int h = e / (kHeadDim + 2), c = e % (kHeadDim + 2);
-      float* dst = a.partial + ((static_cast<size_t>(seq) * a.n_q_heads + kvh * G + h) * a.n_chunks + chunk) * part_stride;
-      dst[c] = (c == kHeadDim) ? -INFINITY : 0.0f;
+      part_ptr(h)[c] = (c == kHeadDim) ? -INFINITY : 0.0f;
     }
     return;
   }
 
-  // ---- issue this wave's value-tile loads first -------------------------------------
-  const int wave_tile0 = wave * kTilesPerWave;  // tile index inside the chunk
-  uint32_t w[kTilesPerWave][kLaneWords];
-  const uint8_t* tiles = a.v_codes + (stream * (S / kTile) + c0 / kTile) * (1024 * VB);
+  if (tid < kNc) cbs[tid] = half_bits_to_float(a.v_cb[tid]);
+  for (int e = tid; e < kPairEntries; e += kThreads)
+    lut2[e] = static_cast<uint32_t>(a.v_cb[e & (kNc - 1)]) | (static_cast<uint32_t>(a.v_cb[e >> VB]) << 16);
+  for (int e = tid; e < kWaves * G * kHeadDim; e += kThreads) (&osp[0][0][0])[e] = 0.0f;
+  __syncthreads();
+  if (tid == 0) zc = cbs[zero_code_index<kNc>(cbs)];
+  __syncthreads();
+
+  // This wave's share of the block's tiles.
+  const int nt = tile_hi - tile_lo;
+  const int w_lo = tile_lo + (nt * wave) / kWaves;
+  const int w_hi = tile_lo + (nt * (wave + 1)) / kWaves;
+
+  const uint8_t* vtiles = a.v_codes + stream * (S / kTile) * (1024 * VB);
+  const float* lbase = a.logits + (static_cast<size_t>(seq) * a.n_q_heads + kvh * G) * S;
+  const bool pf_out = k <= kPrefetchOutliers;
+
+  auto load = [&](int tile, TileData<VB, G>& d) {
+    const uint4* p = reinterpret_cast<const uint4*>(vtiles + static_cast<size_t>(tile) * (1024 * VB) + lane * (16 * VB));
 #pragma unroll
-  for (int tl = 0; tl < kTilesPerWave; ++tl) {
-    if ((wave_tile0 + tl) * kTile < n) {
-      const uint4* p = reinterpret_cast<const uint4*>(tiles + static_cast<size_t>(wave_tile0 + tl) * (1024 * VB) +
-                                                      lane * (16 * VB));
+    for (int v = 0; v < VB; ++v) {
+      const uint4 q = p[v];
+      d.w[4 * v + 0] = q.x;
+      d.w[4 * v + 1] = q.y;
+      d.w[4 * v + 2] = q.z;
+      d.w[4 * v + 3] = q.w;
+    }
+    const int t = tile * kTile + lane;
+    const bool valid = t < L;
+    const size_t slot = stream * S + t;
 #pragma unroll
-      for (int v = 0; v < VB; ++v) {
-        const uint4 d = p[v];
-        w[tl][4 * v + 0] = d.x;
-        w[tl][4 * v + 1] = d.y;
-        w[tl][4 * v + 2] = d.z;
-        w[tl][4 * v + 3] = d.w;
+    for (int h = 0; h < G; ++h) d.lg[h] = valid ? lbase[static_cast<size_t>(h) * S + t] : -INFINITY;
+    d.sv = valid ? a.v_scale[slot] : 0u;
+    d.oi = 0u;
+    d.ov = 0u;
+    if (valid && pf_out) {
+      for (int j = 0; j < k; ++j) {
+        d.oi |= static_cast<uint32_t>(a.v_idx[slot * k + j]) << (8 * j);
+        d.ov |= static_cast<uint32_t>(a.v_val[slot * k + j]) << (16 * j);
       }
     }
-  }
+  };
 
-  for (int e = tid; e < kPairEntries; e += kThreads) lut2[e] = make_float2(a.v_cb[e & (kNc - 1)], a.v_cb[e >> VB]);
-  for (int e = tid; e < G * kHeadDim; e += kThreads) (&osp[0][0])[e] = 0.0f;
-  if (tid == 0) zc = a.v_cb[zero_code_index<kNc>(a.v_cb)];
-
-  // ---- pass 1: max, exp, weights, outlier scatter ----------------------------------
-  float lg[G][kTokPerThread];
-  float mloc[G];
+  float m_run[G], lsum[G], acc[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float* lrow = a.logits + (static_cast<size_t>(seq) * a.n_q_heads + kvh * G + h) * S + c0;
-    mloc[h] = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kTokPerThread; ++u) {
-      const int t = u * kThreads + tid;
-      lg[h][u] = t < n ? lrow[t] : -INFINITY;
-      mloc[h] = fmaxf(mloc[h], lg[h][u]);
-    }
-    mloc[h] = wave_max_f32(mloc[h]);
-    if (lane == 0) red[wave][h] = mloc[h];
+    m_run[h] = -INFINITY;
+    lsum[h] = 0.0f;
+    acc[h][0] = acc[h][1] = 0.0f;
   }
-  __syncthreads();
-  float m[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = red[0][h];
-#pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) m[h] = fmaxf(m[h], red[ww][h]);
-  }
-  __syncthreads();
+  float* my_osp = &osp[wave][0][0];
 
-  float lsum[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) lsum[h] = 0.0f;
-#pragma unroll
-  for (int u = 0; u < kTokPerThread; ++u) {
-    const int t = u * kThreads + tid;
-    const bool valid = t < n;
-    const size_t slot = stream * S + c0 + t;
-    const float s = valid ? half_bits_to_float(a.v_scale[slot]) : 0.0f;
-    float p[G];
+  auto compute = [&](int tile, const TileData<VB, G>& d) {
+    const int t = tile * kTile + lane;
+    const bool valid = t < L;
+    const float s = half_bits_to_float(d.sv);
+    float pr[G], wts[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      p[h] = valid ? expf(lg[h][u] - m[h]) : 0.0f;
-      lsum[h] += p[h];
-      reinterpret_cast<float*>(&wt[h][0])[t] = p[h] * s;
+      const float mt = wave_max_f32(d.lg[h]);
+      if (mt > m_run[h]) {  // wave-uniform: rescale the running state to the new max
+        const float sc = m_run[h] > -INFINITY ? expf(m_run[h] - mt) : 0.0f;
+        m_run[h] = mt;
+        acc[h][0] *= sc;
+        acc[h][1] *= sc;
+        lsum[h] *= sc;
+        my_osp[h * kHeadDim + 2 * lane] *= sc;
+        my_osp[h * kHeadDim + 2 * lane + 1] *= sc;
+      }
+      pr[h] = valid ? expf(d.lg[h] - m_run[h]) : 0.0f;
+      lsum[h] += pr[h];
+      wts[h] = pr[h] * s;
     }
-    if (valid) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (valid && k > 0) {
+      const size_t slot = stream * S + t;
       for (int j = 0; j < k; ++j) {
-        const int c = a.v_idx[slot * k + j];
-        const float dv = half_bits_to_float(a.v_val[slot * k + j]) - zc * s;
+        const int c = pf_out ? ((d.oi >> (8 * j)) & 0xff) : a.v_idx[slot * k + j];
+        const uint32_t vb = pf_out ? ((d.ov >> (16 * j)) & 0xffff) : a.v_val[slot * k + j];
+        const float dv = half_bits_to_float(vb) - zc * s;
 #pragma unroll
-        for (int h = 0; h < G; ++h) atomicAdd(&osp[h][c], p[h] * dv);
+        for (int h = 0; h < G; ++h) atomicAdd(&my_osp[h * kHeadDim + c], pr[h] * dv);
       }
     }
-  }
+    // Dense part: lane = channel pair; the token weights come from lane t as scalars.
+    float accp[G][2][2];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    lsum[h] = wave_sum_f32(lsum[h]);
-    if (lane == 0) red[wave][h] = lsum[h];
-  }
-  __syncthreads();
+    for (int h = 0; h < G; ++h) accp[h][0][0] = accp[h][0][1] = accp[h][1][0] = accp[h][1][1] = 0.0f;
+    static_for<0, kTile / 2>([&](auto mc) {
+      constexpr int mm = decltype(mc)::value;
+      const uint32_t e0 = lut2[field<2 * VB, 2 * VB * mm>(d.w)];
+      const uint32_t e1 = lut2[field<2 * VB, kChanBits + 2 * VB * mm>(d.w)];
+      const float v0a = half_bits_to_float(e0 & 0xffffu), v0b = half_bits_to_float(e0 >> 16);
+      const float v1a = half_bits_to_float(e1 & 0xffffu), v1b = half_bits_to_float(e1 >> 16);
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float wa = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wts[h]), 2 * mm));
+        const float wb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wts[h]), 2 * mm + 1));
+        accp[h][0][mm & 1] = fmaf(v0b, wb, fmaf(v0a, wa, accp[h][0][mm & 1]));
+        accp[h][1][mm & 1] = fmaf(v1b, wb, fmaf(v1a, wa, accp[h][1][mm & 1]));
+      }
+    });
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      acc[h][0] += accp[h][0][0] + accp[h][0][1];
+      acc[h][1] += accp[h][1][0] + accp[h][1][1];
+    }
+  };
 
-  // ---- pass 2: dense product over channel-major tiles -------------------------------
-  float acc[G][2];
-#pragma unroll
-  for (int h = 0; h < G; ++h) acc[h][0] = acc[h][1] = 0.0f;
-#pragma unroll
-  for (int tl = 0; tl < kTilesPerWave; ++tl) {
-    if ((wave_tile0 + tl) * kTile < n) {
-      const float2* wrow = &wt[0][(wave_tile0 + tl) * (kTile / 2)];
-      static_for<0, kTile / 2>([&](auto mc) {
-        constexpr int mm = decltype(mc)::value;
-        const float2 v0 = lut2[field<2 * VB, 2 * VB * mm>(w[tl])];
-        const float2 v1 = lut2[field<2 * VB, kChanBits + 2 * VB * mm>(w[tl])];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float2 ww = wrow[h * (kPvChunk / 2) + mm];
-          acc[h][0] = fmaf(ww.y, v0.y, fmaf(ww.x, v0.x, acc[h][0]));
-          acc[h][1] = fmaf(ww.y, v1.y, fmaf(ww.x, v1.x, acc[h][1]));
-        }
-      });
+  if (w_lo < w_hi) {
+    TileData<VB, G> bufA, bufB;
+    load(w_lo, bufA);
+    for (int tile = w_lo; tile < w_hi; tile += 2) {
+      if (tile + 1 < w_hi) load(tile + 1, bufB);
+      compute(tile, bufA);
+      if (tile + 1 >= w_hi) break;
+      if (tile + 2 < w_hi) load(tile + 2, bufA);
+      compute(tile + 1, bufB);
     }
   }
+
+  // ---- merge the four waves' states -------------------------------------------------
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    part[wave][h][2 * lane] = acc[h][0];
-    part[wave][h][2 * lane + 1] = acc[h][1];
+    const float ls = wave_sum_f32(lsum[h]);
+    if (lane == 0) {
+      wm[wave][h] = m_run[h];
+      wl[wave][h] = ls;
+    }
+    wo[wave][h][2 * lane] = acc[h][0];
+    wo[wave][h][2 * lane + 1] = acc[h][1];
   }
   __syncthreads();
-
   for (int e = tid; e < G * kHeadDim; e += kThreads) {
     const int h = e / kHeadDim, c = e % kHeadDim;
-    float o = osp[h][c];
+    float M = wm[0][h];
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) o += part[ww][h][c];
-    float* dst = a.partial + ((static_cast<size_t>(seq) * a.n_q_heads + kvh * G + h) * a.n_chunks + chunk) * part_stride;
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, wm[w][h]);
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = wm[w][h] > -INFINITY ? expf(wm[w][h] - M) : 0.0f;
+      o += f * (wo[w][h][c] + osp[w][h][c]);
+      l += f * wl[w][h];
+    }
+    float* dst = part_ptr(h);
     dst[c] = o;
     if (c == 0) {
-      float l = 0.0f;
-#pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) l += red[ww][h];
-      dst[kHeadDim] = m[h];
+      dst[kHeadDim] = M;
       dst[kHeadDim + 1] = l;
     }
   }
 }
 
 // One block per (sequence, query head): 256 threads = 128 channels x 2 halves of the
-// chunk list.  Loads are independent, so the chunk loop keeps several in flight.
+// partial list.  Loads are independent, so the loop keeps several in flight.
 __global__ __launch_bounds__(256) void pv_combine_kernel(PvArgs a) {
   __shared__ float red[4];
   __shared__ float acc_n[kHeadDim], acc_d[kHeadDim];
@@ -204,12 +246,13 @@ __global__ __launch_bounds__(256) void pv_combine_kernel(PvArgs a) {
   const int h = blockIdx.x;
   const int seq = blockIdx.y;
   const size_t part_stride = kHeadDim + 2;
-  const float* src = a.partial + (static_cast<size_t>(seq) * a.n_q_heads + h) * a.n_chunks * part_stride;
+  const float* src = a.partial + (static_cast<size_t>(seq) * a.n_q_heads + h) * a.n_parts * part_stride;
   const int L = min(a.seq_len[seq] & kLenMask, a.max_len);
-  const int nc = (L + kPvChunk - 1) / kPvChunk;
+  const int n_tiles = (L + kTile - 1) / kTile;
+  const int np = min(a.n_parts, (n_tiles + a.tiles_per_block - 1) / a.tiles_per_block);
 
   float M = -INFINITY;
-  for (int j = tid; j < nc; j += 256) M = fmaxf(M, src[j * part_stride + kHeadDim]);
+  for (int j = tid; j < np; j += 256) M = fmaxf(M, src[j * part_stride + kHeadDim]);
   M = wave_max_f32(M);
   if ((tid & 63) == 0) red[tid >> 6] = M;
   __syncthreads();
@@ -218,7 +261,7 @@ __global__ __launch_bounds__(256) void pv_combine_kernel(PvArgs a) {
   float num = 0.0f, den = 0.0f;
   if (M > -INFINITY) {
 #pragma unroll 4
-    for (int j = half; j < nc; j += 2) {
+    for (int j = half; j < np; j += 2) {
       const float* pj = src + j * part_stride;
       const float mj = pj[kHeadDim];
       const float wj = mj > -INFINITY ? expf(mj - M) : 0.0f;
@@ -239,8 +282,19 @@ __global__ __launch_bounds__(256) void pv_combine_kernel(PvArgs a) {
 }
 
 template <int VB, int G>
-hipError_t launch_pv_t(int batch, const PvArgs& a, hipStream_t s) {
-  dim3 grid(a.n_chunks, a.n_kv_heads, batch);
+hipError_t launch_pv_t(int batch, const PvArgs& a0, hipStream_t s) {
+  PvArgs a = a0;
+  // One resident round, equal share of block slots per stream, tile-granular runs of at
+  // least kMinTilesPerBlock tiles.
+  const int tiles = (a.max_len + kTile - 1) / kTile;
+  const long streams = static_cast<long>(batch) * a.n_kv_heads;
+  static const int resident = blocks_per_cu(reinterpret_cast<const void*>(&pv_partial_kernel<VB, G>), kThreads);
+  const long slots = static_cast<long>(device_cu_count()) * resident;
+  const long per_stream = std::max(1L, std::min<long>((slots + streams - 1) / streams,
+                                                      (tiles + kMinTilesPerBlock - 1) / kMinTilesPerBlock));
+  a.tiles_per_block = static_cast<int>((tiles + per_stream - 1) / per_stream);
+  a.n_parts = (tiles + a.tiles_per_block - 1) / a.tiles_per_block;
+  dim3 grid(a.n_parts, a.n_kv_heads, batch);
   hipLaunchKernelGGL((pv_partial_kernel<VB, G>), grid, dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

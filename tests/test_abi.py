@@ -44,7 +44,7 @@ def test_cache_sizes_match_layout():
     assert s.v_codes == slots * 128 * 4 // 8
     assert s.k_out_idx == slots * 2 and s.k_out_val == slots * 4
     assert s.v_scale == slots * 2
-    assert s.k_scale == 2 * 128 * 4 and s.k_codebook == 8 * 4 and s.v_codebook == 16 * 4
+    assert s.k_scale == 2 * 128 * 4 and s.k_codebook == 8 * 2 and s.v_codebook == 16 * 2
     assert s.total == sum(getattr(s, f) for f, _ in kvq.Sizes._fields_ if f != "total")
 
 
