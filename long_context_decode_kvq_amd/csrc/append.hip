@@ -22,12 +22,6 @@
 namespace kvq {
 namespace {
 
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
 // Selection key: fp16 magnitude bits above the inverted channel index, so the unsigned
 // maximum is the largest |x| and, among equal magnitudes, the lowest channel.
 __device__ __forceinline__ uint32_t outlier_key(uint32_t xbits, uint32_t c) {
@@ -107,7 +101,7 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
     uint32_t* vtile = reinterpret_cast<uint32_t*>(a.v_codes + (stream * (S / kTile) + tile) * (1024 * VB));
     if (!is_key_wave) {
       for (int i = lane; i < kWave * kLaneWords; i += kWave) vt[i] = vtile[i];
-      wave_sync();
+      wave_lds_sync();
     }
     for (int t = lo; t < hi; ++t) {
       const int j = t - start;  // row of this token in the new-token block
@@ -137,15 +131,15 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
         const float u1 = ks1 > 0.0f ? d1 / ks1 : 0.0f;
         const uint32_t pair = nearest_code<kNcK>(u0, cbk) | (nearest_code<kNcK>(u1, cbk) << KB);
         if (lane < kRecWords) rec[lane] = 0u;
-        wave_sync();
+        wave_lds_sync();
         const int bit = 2 * KB * lane;
         const int w = bit >> 5;
         const int sh = bit & 31;
         atomicOr(&rec[w], pair << sh);
         if (sh + 2 * KB > 32) atomicOr(&rec[w + 1], pair >> (32 - sh));
-        wave_sync();
+        wave_lds_sync();
         if (lane < kRecWords) reinterpret_cast<uint32_t*>(a.k_codes + slot * (16 * KB))[lane] = rec[lane];
-        wave_sync();
+        wave_lds_sync();
       } else {
         // ---- value: channels (2 lane, 2 lane + 1), one scale per vector --------------
         const uint32_t xx = reinterpret_cast<const uint32_t*>(a.v_new + src)[lane];
@@ -191,9 +185,9 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
       }
     }
     if (!is_key_wave) {
-      wave_sync();
+      wave_lds_sync();
       for (int i = lane; i < kWave * kLaneWords; i += kWave) vtile[i] = vt[i];
-      wave_sync();
+      wave_lds_sync();
     }
   }
 }

@@ -181,7 +181,9 @@ int kvq_qk_matvec(const kvq_shape* s, const kvq_cache* c, const void* q, int32_t
   a.max_len = max_len;
   a.q_is_fp16 = q_is_fp16;
   a.sm_scale = sm_scale;
-  a.theta_log2 = std::log2(static_cast<double>(s->rope_base)) * 2.0 / s->head_dim;
+  // theta_i = base^(-2i/D); stored in revolutions so that the kernels reduce phases exactly
+  const double theta_log2 = std::log2(static_cast<double>(s->rope_base)) * 2.0 / s->head_dim;
+  for (int i = 0; i < kvq::kHalf; ++i) a.theta_rev[i] = std::exp2(-i * theta_log2) / (2.0 * M_PI);
   a.q = q;
   a.k_codes = c->k_codes;
   a.k_idx = c->k_out_idx;

@@ -18,25 +18,52 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
 
+// Orders this wave's LDS writes before its later LDS reads of other lanes' entries.  A
+// wave's LDS operations execute in order, so wavefront-scope fences suffice: they emit
+// no wait on outstanding global loads, which keeps prefetched tiles in flight.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Wave reductions: four DPP steps combine the 16 lanes of each row (xor 1, xor 2, half-row
+// mirror, row mirror), then the four row results are read into scalar registers.  Every
+// lane gets the result; no LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xf, 0xf, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, dpp_u32<CTRL>(__builtin_bit_cast(uint32_t, v)));
+}
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int l) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+}
+__device__ __forceinline__ float lane_f32(float v, int l) {
+  return __builtin_bit_cast(float, lane_u32(__builtin_bit_cast(uint32_t, v), l));
+}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t o = __shfl_xor(v, off, kWave);
-    v = v > o ? v : o;
-  }
-  return v;
+  v = max(v, dpp_u32<0xB1>(v));
+  v = max(v, dpp_u32<0x4E>(v));
+  v = max(v, dpp_u32<0x141>(v));
+  v = max(v, dpp_u32<0x140>(v));
+  return max(max(lane_u32(v, 0), lane_u32(v, 16)), max(lane_u32(v, 32), lane_u32(v, 48)));
 }
-
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  return v;
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
 }
-
 __device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
 }
 
 // b-bit field starting at compile-time bit position POS of a little-endian stream held in
@@ -83,18 +110,26 @@ __device__ __forceinline__ uint32_t nearest_code(float u, const float* cb) {
 
 // Index of the codebook entry nearest to 0 (the code of every dense-zero entry, in
 // particular of every outlier slot): smallest j minimising |0 - cb[j]|.
+// Block barrier for data exchanged through LDS only.  It waits for this wave's LDS
+// operations and then for every wave of the block, but not for outstanding global loads
+// (a workgroup-scope fence, as in __syncthreads, drains those too), so prefetched tiles
+// stay in flight across it.  The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void block_lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Value of the codebook entry nearest zero (the lowest index among equal magnitudes):
+// the dense value stored at an outlier's channel.  Lane j < NC passes the fp16 bits of
+// entry j; fp16 magnitudes order as integers like the numbers they encode.  Every lane of
+// the wave gets the value.
 template <int NC>
-__device__ __forceinline__ int zero_code_index(const float* cb) {
-  int j0 = 0;
-  float bd = fabsf(0.0f - cb[0]);
-  for (int j = 1; j < NC; ++j) {
-    const float d = fabsf(0.0f - cb[j]);
-    if (d < bd) {
-      bd = d;
-      j0 = j;
-    }
-  }
-  return j0;
+__device__ __forceinline__ float zero_code_value(uint32_t cb_bits, int lane) {
+  const uint32_t key = lane < NC ? ((cb_bits & 0x7fffu) << 8) | static_cast<uint32_t>(lane) : 0xffffffffu;
+  const uint32_t m = ~wave_max_u32(~key);  // wave minimum
+  return half_bits_to_float(static_cast<uint32_t>(__shfl(static_cast<int>(cb_bits), static_cast<int>(m & 0xffu))) & 0xffffu);
 }
 
 // cos/sin of 2*pi*r for a revolution count r already reduced to [0, 1).

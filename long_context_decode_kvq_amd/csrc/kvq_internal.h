@@ -36,7 +36,7 @@ struct QkArgs {
   int32_t n_q_heads, n_kv_heads, max_seq, n_outliers, max_len, q_is_fp16;
   int32_t tiles_per_wave;  // set by the launcher
   float sm_scale;
-  double theta_log2;  // log2(rope_base) * 2 / head_dim: theta_i = 2^(-i * theta_log2)
+  double theta_rev[kHalf];  // theta_i / 2pi for the 64 rotary pairs, from the host in float64
   const void* q;
   const uint8_t* k_codes;
   const uint8_t* k_idx;

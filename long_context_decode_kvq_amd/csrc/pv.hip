@@ -37,7 +37,7 @@ struct TileData {
   uint32_t w[4 * VB];  // this lane's value-tile words (channels 2l, 2l+1)
   float lg[G];         // logit of token `lane` for every query head of the group
   uint32_t sv;         // fp16 value scale of token `lane`
-  uint32_t oi, ov;     // its first two outliers: channels (u8 x2) and fp16 values
+  uint32_t oi[2], ov[2];  // its first two outliers: channels and fp16 value bits
 };
 
 template <int VB, int G>
@@ -47,15 +47,13 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   constexpr int kPairEntries = 1 << (2 * VB);
 
   __shared__ uint32_t lut2[kPairEntries];         // fp16 (cb[a], cb[b]) for a token pair
-  __shared__ float cbs[kNc];
   __shared__ float osp[kWaves][G][kHeadDim];      // per-wave outlier corrections
   __shared__ float wm[kWaves][G], wl[kWaves][G];  // per-wave max and sum
   __shared__ float wo[kWaves][G][kHeadDim];       // per-wave weighted sums
-  __shared__ float zc;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int kvh = blockIdx.y;
   const int seq = blockIdx.z;
   const int H = a.n_kv_heads;
@@ -79,14 +77,6 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
     return;
   }
 
-  if (tid < kNc) cbs[tid] = half_bits_to_float(a.v_cb[tid]);
-  for (int e = tid; e < kPairEntries; e += kThreads)
-    lut2[e] = static_cast<uint32_t>(a.v_cb[e & (kNc - 1)]) | (static_cast<uint32_t>(a.v_cb[e >> VB]) << 16);
-  for (int e = tid; e < kWaves * G * kHeadDim; e += kThreads) (&osp[0][0][0])[e] = 0.0f;
-  __syncthreads();
-  if (tid == 0) zc = cbs[zero_code_index<kNc>(cbs)];
-  __syncthreads();
-
   // This wave's share of the block's tiles.
   const int nt = tile_hi - tile_lo;
   const int w_lo = tile_lo + (nt * wave) / kWaves;
@@ -94,9 +84,19 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
 
   const uint8_t* vtiles = a.v_codes + stream * (S / kTile) * (1024 * VB);
   const float* lbase = a.logits + (static_cast<size_t>(seq) * a.n_q_heads + kvh * G) * S;
-  const bool pf_out = k <= kPrefetchOutliers;
+  // The first kPrefetchOutliers outliers of every token travel with its tile data; with
+  // fewer outliers the spare loads repeat a real one or read the first code word, and
+  // their results are ignored.
+  const int kp = min(k, kPrefetchOutliers);
+  const uint8_t* o_idx = kp > 0 ? a.v_idx : a.v_codes;
+  const uint16_t* o_val = kp > 0 ? a.v_val : reinterpret_cast<const uint16_t*>(a.v_codes);
+  const size_t o_stride = kp > 0 ? k : 0;
+  const int o_second = kp > 1 ? 1 : 0;
 
+  // Every call issues the same loads (a tile past the wave's run reloads its last tile,
+  // a cache hit), so the compiler can wait for exactly the tile being consumed.
   auto load = [&](int tile, TileData<VB, G>& d) {
+    tile = max(0, min(tile, w_hi - 1));  // a wave without tiles reads tile 0 (always valid)
     const uint4* p = reinterpret_cast<const uint4*>(vtiles + static_cast<size_t>(tile) * (1024 * VB) + lane * (16 * VB));
 #pragma unroll
     for (int v = 0; v < VB; ++v) {
@@ -106,21 +106,34 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
       d.w[4 * v + 2] = q.z;
       d.w[4 * v + 3] = q.w;
     }
-    const int t = tile * kTile + lane;
-    const bool valid = t < L;
+    const int t = tile * kTile + lane;  // < max_seq, so every load below is in bounds
     const size_t slot = stream * S + t;
 #pragma unroll
-    for (int h = 0; h < G; ++h) d.lg[h] = valid ? lbase[static_cast<size_t>(h) * S + t] : -INFINITY;
-    d.sv = valid ? a.v_scale[slot] : 0u;
-    d.oi = 0u;
-    d.ov = 0u;
-    if (valid && pf_out) {
-      for (int j = 0; j < k; ++j) {
-        d.oi |= static_cast<uint32_t>(a.v_idx[slot * k + j]) << (8 * j);
-        d.ov |= static_cast<uint32_t>(a.v_val[slot * k + j]) << (16 * j);
-      }
-    }
+    for (int h = 0; h < G; ++h) d.lg[h] = lbase[static_cast<size_t>(h) * S + t];
+    d.sv = a.v_scale[slot];
+    const uint8_t* i0 = o_idx + slot * o_stride;
+    const uint16_t* v0 = o_val + slot * o_stride;
+    d.oi[0] = i0[0];
+    d.oi[1] = i0[o_second];
+    d.ov[0] = v0[0];
+    d.ov[1] = v0[o_second];
   };
+
+  // Set-up inputs first, then the wave's first tile, so that the tile's memory latency
+  // overlaps the set-up and waiting for the inputs never waits for the tile (global loads
+  // complete in issue order).
+  static_assert(kPairEntries <= kThreads, "one table entry per thread");
+  const uint32_t cb_a = a.v_cb[tid & (kNc - 1)];
+  const uint32_t cb_b = a.v_cb[(tid >> VB) & (kNc - 1)];
+  const uint32_t cb_lo = a.v_cb[lane & (kNc - 1)];
+  TileData<VB, G> bufA, bufB;
+  load(w_lo, bufA);  // unconditional, so the compiler counts the loads in flight exactly
+
+  lut2[tid & (kPairEntries - 1)] = cb_a | (cb_b << 16);  // threads sharing an entry write the same value
+  for (int e = tid; e < kWaves * G * kHeadDim; e += kThreads) (&osp[0][0][0])[e] = 0.0f;
+  const float zc = zero_code_value<kNc>(cb_lo, lane);  // value every outlier slot decodes to
+  block_lds_barrier();
+
 
   float m_run[G], lsum[G], acc[G][2];
 #pragma unroll
@@ -138,7 +151,8 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
     float pr[G], wts[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mt = wave_max_f32(d.lg[h]);
+      const float lg = valid ? d.lg[h] : -INFINITY;
+      const float mt = wave_max_f32(lg);
       if (mt > m_run[h]) {  // wave-uniform: rescale the running state to the new max
         const float sc = m_run[h] > -INFINITY ? expf(m_run[h] - mt) : 0.0f;
         m_run[h] = mt;
@@ -148,22 +162,24 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
         my_osp[h * kHeadDim + 2 * lane] *= sc;
         my_osp[h * kHeadDim + 2 * lane + 1] *= sc;
       }
-      pr[h] = valid ? expf(d.lg[h] - m_run[h]) : 0.0f;
+      pr[h] = valid ? expf(lg - m_run[h]) : 0.0f;
       lsum[h] += pr[h];
       wts[h] = pr[h] * s;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    if (valid && k > 0) {
-      const size_t slot = stream * S + t;
-      for (int j = 0; j < k; ++j) {
-        const int c = pf_out ? ((d.oi >> (8 * j)) & 0xff) : a.v_idx[slot * k + j];
-        const uint32_t vb = pf_out ? ((d.ov >> (16 * j)) & 0xffff) : a.v_val[slot * k + j];
-        const float dv = half_bits_to_float(vb) - zc * s;
+    wave_lds_sync();
+    // Outliers: the dense code at an outlier channel is the zero code, so add
+    // p_t * (x_c - zc * s_t) to channel c.
+    auto add_outlier = [&](int c, uint32_t vbits) {
+      c &= kHeadDim - 1;  // a token past the length may hold stale bytes
+      const float dv = half_bits_to_float(vbits) - zc * s;
 #pragma unroll
-        for (int h = 0; h < G; ++h) atomicAdd(&my_osp[h * kHeadDim + c], pr[h] * dv);
-      }
+      for (int h = 0; h < G; ++h) atomicAdd(&my_osp[h * kHeadDim + c], pr[h] * dv);
+    };
+    if (kp >= 1) add_outlier(d.oi[0], d.ov[0]);
+    if (kp >= 2) add_outlier(d.oi[1], d.ov[1]);
+    if (valid) {
+      const size_t slot = stream * S + t;
+      for (int j = kPrefetchOutliers; j < k; ++j) add_outlier(a.v_idx[slot * k + j], a.v_val[slot * k + j]);
     }
     // Dense part: lane = channel pair; the token weights come from lane t as scalars.
     float accp[G][2][2];
@@ -191,13 +207,11 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   };
 
   if (w_lo < w_hi) {
-    TileData<VB, G> bufA, bufB;
-    load(w_lo, bufA);
     for (int tile = w_lo; tile < w_hi; tile += 2) {
-      if (tile + 1 < w_hi) load(tile + 1, bufB);
+      load(tile + 1, bufB);
       compute(tile, bufA);
       if (tile + 1 >= w_hi) break;
-      if (tile + 2 < w_hi) load(tile + 2, bufA);
+      load(tile + 2, bufA);
       compute(tile + 1, bufB);
     }
   }
@@ -213,7 +227,7 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
     wo[wave][h][2 * lane] = acc[h][0];
     wo[wave][h][2 * lane + 1] = acc[h][1];
   }
-  __syncthreads();
+  block_lds_barrier();
   for (int e = tid; e < G * kHeadDim; e += kThreads) {
     const int h = e / kHeadDim, c = e % kHeadDim;
     float M = wm[0][h];

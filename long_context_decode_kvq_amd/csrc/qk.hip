@@ -60,6 +60,13 @@ __device__ __forceinline__ float pair_term(float acc, uint32_t e2, float er, flo
 }
 
 constexpr int kWaves = 4;
+constexpr int kPrefetchOutliers = 2;  // outliers per token fetched with the record
+
+template <int KB>
+struct Rec {
+  uint32_t w[4 * KB];  // the token's key record
+  uint32_t oi[2], ov[2];  // its first two outliers: channels and fp16 value bits
+};
 constexpr int kPartials = 4;  // partial sums per logit
 constexpr int kRegPairs = KVQ_QK_REG_PAIRS;
 static_assert(kRegPairs >= 0 && kRegPairs <= kHalf, "register pairs out of range");
@@ -76,12 +83,12 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   __shared__ float ks[kHeadDim];
   __shared__ float2 ksp[kHalf];             // (s_i, s_{i+64})
   __shared__ float2 qr[kWaves][G][kHalf];   // per-wave tile-rotated query pairs
-  __shared__ float cbs[kNc];
-  __shared__ float zc;                      // value every outlier slot decodes to
+  __shared__ float2 tb[kWaves][kHalf];      // per wave: R(t0 theta_i) at its first tile
+  __shared__ float2 tstep[kHalf];           // R(64 theta_i), the step between tiles
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int kvh = blockIdx.y;
   const int seq = blockIdx.z;
   const int H = a.n_kv_heads;
@@ -91,14 +98,101 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   const int block_tile0 = blockIdx.x * a.tiles_per_wave * kWaves;
   if (block_tile0 * kTile >= L) return;
 
+  const int wave_tile0 = block_tile0 + wave * a.tiles_per_wave;
+  const int n_tiles = min(a.tiles_per_wave, (L - wave_tile0 * kTile + kTile - 1) / kTile);
+  const size_t stream = static_cast<size_t>(seq) * H + kvh;
+  const uint8_t* recs = a.k_codes + stream * S * (16 * KB);
+  // last tile a prefetch may touch; a wave without tiles reads tile 0 (always valid)
+  const int last_tile = n_tiles > 0 ? wave_tile0 + n_tiles - 1 : 0;
+  // The first kPrefetchOutliers outliers of every token travel with its record; with
+  // fewer outliers the spare loads repeat a real one or read the first code word, and
+  // their results are ignored.
+  const int kp = min(k, kPrefetchOutliers);
+  const uint8_t* o_idx = kp > 0 ? a.k_idx : a.k_codes;
+  const uint16_t* o_val = kp > 0 ? a.k_val : reinterpret_cast<const uint16_t*>(a.k_codes);
+  const size_t o_stride = kp > 0 ? k : 0;
+  const int o_second = kp > 1 ? 1 : 0;
+
+  auto load_rec = [&](int tile, Rec<KB>& d) {
+    tile = min(tile, last_tile);  // past the run: reload the last tile (cache hit), keeps the load count fixed
+    const size_t slot = stream * S + static_cast<size_t>(tile) * kTile + lane;
+    const uint4* p = reinterpret_cast<const uint4*>(recs + (static_cast<size_t>(tile) * kTile + lane) * (16 * KB));
+#pragma unroll
+    for (int v = 0; v < KB; ++v) {
+      const uint4 q = p[v];
+      d.w[4 * v + 0] = q.x;
+      d.w[4 * v + 1] = q.y;
+      d.w[4 * v + 2] = q.z;
+      d.w[4 * v + 3] = q.w;
+    }
+    const uint8_t* i0 = o_idx + slot * o_stride;
+    const uint16_t* v0 = o_val + slot * o_stride;
+    d.oi[0] = i0[0];
+    d.oi[1] = i0[o_second];
+    d.ov[0] = v0[0];
+    d.ov[1] = v0[o_second];
+  };
+
+  // Query pairs this lane rotates every tile.  Slot j holds rotary pair
+  // (lane & 15) + 16 j, so lane n of every 16-lane row holds the pairs congruent to n mod
+  // 16 and a row broadcast hands pair i's coefficient to all lanes.  The pair `lane` itself
+  // (needed in LDS) is slot lane >> 4.
+  constexpr int kSlots = kHalf / 16;
+  // Raw query words (fp16 or fp32 bits), converted only after the tile prefetch is issued.
+  uint32_t ra[kSlots][G], rb[kSlots][G];
+  const size_t q0 = (static_cast<size_t>(seq) * a.n_q_heads + kvh * G) * kHeadDim + (lane & 15);
+  if (a.q_is_fp16) {  // wave-uniform; both paths issue the same loads
+    const uint16_t* q16 = static_cast<const uint16_t*>(a.q) + q0;
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        ra[j][h] = q16[h * kHeadDim + 16 * j];
+        rb[j][h] = q16[h * kHeadDim + 16 * j + kHalf];
+      }
+  } else {
+    const uint32_t* q32 = static_cast<const uint32_t*>(a.q) + q0;
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        ra[j][h] = q32[h * kHeadDim + 16 * j];
+        rb[j][h] = q32[h * kHeadDim + 16 * j + kHalf];
+      }
+  }
+  // Set-up inputs, loaded ahead of the tile prefetch so that waiting for them never
+  // waits for the prefetch (global loads complete in issue order).
+  // Every thread writes its table entries (indices masked, so threads that share an entry
+  // write the same value): no load is guarded by a branch the compiler could sink it into.
+  const float ks_own = a.k_scale[kvh * kHeadDim + (tid & (kHeadDim - 1))];
+  const float ks_lo = a.k_scale[kvh * kHeadDim + (tid & (kHalf - 1))];
+  const float ks_hi = a.k_scale[kvh * kHeadDim + (tid & (kHalf - 1)) + kHalf];
+  const uint32_t cb_lo = a.k_cb[lane & (kNc - 1)];
+  static_assert(kPairEntries <= 256, "one table entry per thread");
+  const uint32_t cb_pa = a.k_cb[tid & (kNc - 1)];
+  const uint32_t cb_pb = a.k_cb[(tid >> KB) & (kNc - 1)];
+  const double th_rev = a.theta_rev[lane];
+
+  // The first two tiles are requested before the tables are built, so their memory
+  // latency overlaps the set-up.
+  // Every load here is unconditional (clamped addresses), so the compiler can count the
+  // loads in flight exactly and wait only for the ones it needs.
+  Rec<KB> r0, r1, r2;
+  load_rec(wave_tile0, r0);
+  load_rec(wave_tile0 + 1, r1);
+
   // ---- per-block tables -----------------------------------------------------------
-  if (tid < kHeadDim) ks[tid] = a.k_scale[kvh * kHeadDim + tid];
-  if (tid < kHalf) ksp[tid] = make_float2(a.k_scale[kvh * kHeadDim + tid], a.k_scale[kvh * kHeadDim + tid + kHalf]);
-  if (tid < kNc) cbs[tid] = half_bits_to_float(a.k_cb[tid]);
-  for (int e = tid; e < kPairEntries; e += 256)
-    lutp[e] = static_cast<uint32_t>(a.k_cb[e & (kNc - 1)]) | (static_cast<uint32_t>(a.k_cb[e >> KB]) << 16);
-  const double inv2pi = 0.15915494309189533577;
-  const double th_rev = exp2(-static_cast<double>(lane) * a.theta_log2) * inv2pi;  // theta_lane / 2pi
+  ks[tid & (kHeadDim - 1)] = ks_own;
+  ksp[tid & (kHalf - 1)] = make_float2(ks_lo, ks_hi);
+  lutp[tid & (kPairEntries - 1)] = cb_pa | (cb_pb << 16);
+  float qa[kSlots][G], qb[kSlots][G];
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      qa[j][h] = a.q_is_fp16 ? half_bits_to_float(ra[j][h]) : __builtin_bit_cast(float, ra[j][h]);
+      qb[j][h] = a.q_is_fp16 ? half_bits_to_float(rb[j][h]) : __builtin_bit_cast(float, rb[j][h]);
+    }
   {
     // 16 consecutive tau of pair `lane` per thread: one accurate seed angle, then steps by
     // the single-step rotation (<= 15 float32 rotations).
@@ -115,36 +209,29 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
       s0 = sn;
     }
   }
-  // Query pairs this lane rotates every tile.  Slot j holds rotary pair
-  // (lane & 15) + 16 j, so lane n of every 16-lane row holds the pairs congruent to n mod
-  // 16 and a row broadcast hands pair i's coefficient to all lanes.  The pair `lane` itself
-  // (needed in LDS) is slot lane >> 4.
-  constexpr int kSlots = kHalf / 16;
-  float qa[kSlots][G], qb[kSlots][G];
+  {
+    // pair `lane`: its phase at the wave's first tile, and the per-tile step
+    float sb, cb, sst, cst;
+    sincos_rev(frac_rev(static_cast<double>(wave_tile0) * kTile, th_rev), &sb, &cb);
+    sincos_rev(frac_rev(static_cast<double>(kTile), th_rev), &sst, &cst);
+    tb[wave][lane] = make_float2(cb, sb);
+    tstep[lane] = make_float2(cst, sst);  // every wave writes the same value
+  }
+  // value every outlier slot decodes to: the codebook entry nearest zero
+  const float zc = zero_code_value<kNc>(cb_lo, lane);
+  block_lds_barrier();
+  float s_lo[kSlots], s_hi[kSlots];  // scales of the slot pairs
+  float bc[kSlots], bs[kSlots], sc[kSlots], ss[kSlots];  // their tile-base phase and per-tile step
 #pragma unroll
   for (int j = 0; j < kSlots; ++j) {
     const int pr = (lane & 15) + 16 * j;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const size_t qi = (static_cast<size_t>(seq) * a.n_q_heads + kvh * G + h) * kHeadDim + pr;
-      if (a.q_is_fp16) {
-        const uint16_t* q16 = static_cast<const uint16_t*>(a.q);
-        qa[j][h] = half_bits_to_float(q16[qi]);
-        qb[j][h] = half_bits_to_float(q16[qi + kHalf]);
-      } else {
-        const float* q32 = static_cast<const float*>(a.q);
-        qa[j][h] = q32[qi];
-        qb[j][h] = q32[qi + kHalf];
-      }
-    }
-  }
-  __syncthreads();
-  if (tid == 0) zc = cbs[zero_code_index<kNc>(cbs)];
-  float s_lo[kSlots], s_hi[kSlots];  // scales of the slot pairs
-#pragma unroll
-  for (int j = 0; j < kSlots; ++j) {
-    s_lo[j] = ks[(lane & 15) + 16 * j];
-    s_hi[j] = ks[(lane & 15) + 16 * j + kHalf];
+    s_lo[j] = ks[pr];
+    s_hi[j] = ks[pr + kHalf];
+    const float2 b = tb[wave][pr], st = tstep[pr];
+    bc[j] = b.x;
+    bs[j] = b.y;
+    sc[j] = st.x;
+    ss[j] = st.y;
   }
 
   // R(tau) for this lane's token: the first kRegPairs pairs in registers.
@@ -155,42 +242,15 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
     er[i] = e.x;
     ei[i] = e.y;
   }
-  __syncthreads();
+  if (n_tiles <= 0) return;  // after the block's last barrier
 
-  const int wave_tile0 = block_tile0 + wave * a.tiles_per_wave;
-  const int n_tiles = min(a.tiles_per_wave, (L - wave_tile0 * kTile + kTile - 1) / kTile);
-  if (n_tiles <= 0) return;
-
-  // tile-base phase of every slot pair for the wave's first tile, and its per-tile step
-  float bc[kSlots], bs[kSlots], sc[kSlots], ss[kSlots];
-#pragma unroll
-  for (int j = 0; j < kSlots; ++j) {
-    const double thj = exp2(-static_cast<double>((lane & 15) + 16 * j) * a.theta_log2) * inv2pi;
-    sincos_rev(frac_rev(static_cast<double>(wave_tile0) * kTile, thj), &bs[j], &bc[j]);
-    sincos_rev(frac_rev(static_cast<double>(kTile), thj), &ss[j], &sc[j]);
-  }
   const int my_slot = lane >> 4;
   static_assert(kSlots == 4, "four 16-lane rows");
   auto pick = [&](float v0, float v1, float v2, float v3) {
     return my_slot == 0 ? v0 : my_slot == 1 ? v1 : my_slot == 2 ? v2 : v3;
   };
 
-  const size_t stream = static_cast<size_t>(seq) * H + kvh;
-  const uint8_t* recs = a.k_codes + stream * S * (16 * KB);
-
-  auto load_rec = [&](int tile, uint32_t (&w)[kRecWords]) {
-    const uint4* p = reinterpret_cast<const uint4*>(recs + (static_cast<size_t>(tile) * kTile + lane) * (16 * KB));
-#pragma unroll
-    for (int v = 0; v < KB; ++v) {
-      const uint4 d = p[v];
-      w[4 * v + 0] = d.x;
-      w[4 * v + 1] = d.y;
-      w[4 * v + 2] = d.z;
-      w[4 * v + 3] = d.w;
-    }
-  };
-
-  auto process = [&](int tile, const uint32_t (&r)[kRecWords]) {
+  auto process = [&](int tile, const Rec<KB>& d) {
     // q' = R(-t0) q for the slot pairs of every head, then step the base phases.
     float alp[kSlots], bet[kSlots], gam[kSlots], ndl[kSlots];
 #pragma unroll
@@ -225,9 +285,7 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
       bc[j] = nc;
       bs[j] = ns;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    wave_lds_sync();
 
     const int t = tile * kTile + lane;
     // Independent partial sums keep the FMA chains short, so the scheduler interleaves
@@ -240,7 +298,7 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
 
     static_for<0, kHalf>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      const uint32_t e2 = lutp[field<2 * KB, 2 * KB * i>(r)];
+      const uint32_t e2 = lutp[field<2 * KB, 2 * KB * i>(d.w)];
       float cr, ci;
       if constexpr (i < kRegPairs) {
         cr = er[i];
@@ -279,20 +337,23 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
 
     // Outliers: the record holds the zero code at each outlier channel; replace its
     // decoded value zc * s_c by the stored fp16 value.
+    auto add_outlier = [&](int c, uint32_t vbits) {
+      c &= kHeadDim - 1;  // a token past the length may hold stale bytes
+      const float dv = half_bits_to_float(vbits) - zc * ks[c];
+      const int i = c & (kHalf - 1);
+      const float2 e = et[i][lane];
+      const bool upper = c >= kHalf;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float2 qq = qr[wave][h][i];
+        acc[h] += dv * (upper ? (qq.y * e.x - qq.x * e.y) : (qq.x * e.x + qq.y * e.y));
+      }
+    };
+    if (kp >= 1) add_outlier(d.oi[0], d.ov[0]);
+    if (kp >= 2) add_outlier(d.oi[1], d.ov[1]);
     if (t < L) {
       const size_t o = (stream * S + t) * k;
-      for (int j = 0; j < k; ++j) {
-        const int c = a.k_idx[o + j];
-        const float dv = half_bits_to_float(a.k_val[o + j]) - zc * ks[c];
-        const int i = c & (kHalf - 1);
-        const float2 e = et[i][lane];
-        const bool upper = c >= kHalf;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float2 qq = qr[wave][h][i];
-          acc[h] += dv * (upper ? (qq.y * e.x - qq.x * e.y) : (qq.x * e.x + qq.y * e.y));
-        }
-      }
+      for (int j = kPrefetchOutliers; j < k; ++j) add_outlier(a.k_idx[o + j], a.k_val[o + j]);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         a.logits[(static_cast<size_t>(seq) * a.n_q_heads + kvh * G + h) * S + t] = a.sm_scale * acc[h];
@@ -301,18 +362,15 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Three record buffers: the tiles it+1 and it+2 are in flight while tile it is used.
-  uint32_t r0[kRecWords], r1[kRecWords], r2[kRecWords];
-  load_rec(wave_tile0, r0);
-  if (n_tiles > 1) load_rec(wave_tile0 + 1, r1);
+  // Three buffers: the tiles it+1 and it+2 are in flight while tile it is used.
   for (int it = 0; it < n_tiles; it += 3) {
-    if (it + 2 < n_tiles) load_rec(wave_tile0 + it + 2, r2);
+    load_rec(wave_tile0 + it + 2, r2);
     process(wave_tile0 + it, r0);
     if (it + 1 >= n_tiles) break;
-    if (it + 3 < n_tiles) load_rec(wave_tile0 + it + 3, r0);
+    load_rec(wave_tile0 + it + 3, r0);
     process(wave_tile0 + it + 1, r1);
     if (it + 2 >= n_tiles) break;
-    if (it + 4 < n_tiles) load_rec(wave_tile0 + it + 4, r1);
+    load_rec(wave_tile0 + it + 4, r1);
     process(wave_tile0 + it + 2, r2);
   }
 }
