@@ -183,7 +183,13 @@ int kvq_qk_matvec(const kvq_shape* s, const kvq_cache* c, const void* q, int32_t
   a.sm_scale = sm_scale;
   // theta_i = base^(-2i/D); stored in revolutions so that the kernels reduce phases exactly
   const double theta_log2 = std::log2(static_cast<double>(s->rope_base)) * 2.0 / s->head_dim;
-  for (int i = 0; i < kvq::kHalf; ++i) a.theta_rev[i] = std::exp2(-i * theta_log2) / (2.0 * M_PI);
+  for (int i = 0; i < kvq::kHalf; ++i) {
+    a.theta_rev[i] = std::exp2(-i * theta_log2) / (2.0 * M_PI);
+    int e = 0;
+    const double m = std::frexp(a.theta_rev[i], &e);  // theta_rev = m 2^e, m in [0.5, 1)
+    a.th_hi[i] = static_cast<float>(std::ldexp(std::nearbyint(std::ldexp(m, 15)), e - 15));
+    a.th_lo[i] = static_cast<float>(a.theta_rev[i] - static_cast<double>(a.th_hi[i]));
+  }
   a.q = q;
   a.k_codes = c->k_codes;
   a.k_idx = c->k_out_idx;
@@ -192,6 +198,9 @@ int kvq_qk_matvec(const kvq_shape* s, const kvq_cache* c, const void* q, int32_t
   a.k_cb = c->k_codebook;
   a.seq_len = c->seq_len;
   a.logits = logits;
+  // One query head per kv head: the table-driven kernel for 2- and 3-bit keys (its 4-bit
+  // table, 256 code pairs per rotary pair, costs more to rebuild than it saves).
+  if (s->n_q_heads == s->n_kv_heads && s->k_bits <= 3) return hip_status(kvq::launch_qk_lut(s->k_bits, s->batch, a, stream));
   return hip_status(kvq::launch_qk(s->k_bits, s->n_q_heads / s->n_kv_heads, s->batch, a, stream));
 }
 

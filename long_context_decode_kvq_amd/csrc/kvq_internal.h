@@ -37,6 +37,8 @@ struct QkArgs {
   int32_t tiles_per_wave;  // set by the launcher
   float sm_scale;
   double theta_rev[kHalf];  // theta_i / 2pi for the 64 rotary pairs, from the host in float64
+  float th_hi[kHalf];       // theta_rev rounded to 15 significant bits: tau * th_hi is exact for tau < 512
+  float th_lo[kHalf];       // theta_rev - th_hi
   const void* q;
   const uint8_t* k_codes;
   const uint8_t* k_idx;
@@ -74,6 +76,7 @@ inline int blocks_per_cu(const void* kernel, int threads) {
 
 hipError_t launch_append(int k_bits, int v_bits, const AppendArgs& a, hipStream_t s);
 hipError_t launch_qk(int k_bits, int group, int batch, const QkArgs& a, hipStream_t s);
+hipError_t launch_qk_lut(int k_bits, int batch, const QkArgs& a, hipStream_t s);
 hipError_t launch_pv(int v_bits, int group, int batch, const PvArgs& a, hipStream_t s);
 
 }  // namespace kvq
