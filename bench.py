@@ -33,8 +33,15 @@ def parse():
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-heads", type=int, default=24, help="kv-head streams the oracle times in the CPU leg")
-    p.add_argument("--kernel-steps", type=int, default=5, help="eager steps timed per kernel for the roofline")
+    p.add_argument("--cpu-heads", type=int, default=32, help="kv-head streams per layer the oracle times in the CPU leg")
+    p.add_argument("--cpu-layers", type=int, default=4, help="layers the oracle times in the CPU leg")
+    p.add_argument("--kernel-steps", type=int, default=5,
+                   help="rounds of back-to-back launches (one per layer) timed per entry point for the roofline")
+    p.add_argument("--traffic-probe", action="store_true",
+                   help="after the run, launch a 256 MiB int32 bitwise_not (known bytes) to calibrate HBM counters")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="write profiles/traffic.json from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script "
+                        "with --traffic-probe, then exit")
     p.add_argument("--no-graph", dest="graph", action="store_false",
                    help="launch every kernel eagerly instead of replaying one HIP graph per step")
     return p.parse_args()
@@ -76,49 +83,105 @@ def traffic_from_profile(kernel, src_hash):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, seed, n_heads):
+PROBE_BYTES = 256 << 20  # the calibration kernel reads and writes this many bytes
+
+
+def counter_means(d, counter):
+    """Mean value of `counter` per dispatch, by kernel, from rocprofv3 counter CSVs under d."""
+    import csv
+    import glob
+    import re
+    acc = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row.get("Counter_Name") != counter:
+                continue
+            m = re.search(r"(qk_lut_kernel|qk_kernel|pv_partial_kernel|pv_combine_kernel|append_kernel|bitwise_not)",
+                          row.get("Kernel_Name", ""))
+            if m:
+                acc.setdefault(m.group(1), []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """HBM bytes per launch = FETCH_SIZE and WRITE_SIZE (KiB per dispatch) each scaled by the
+    factor that maps the same counter of the calibration kernel onto its known bytes."""
+    fetch, write = counter_means(fetch_dir, "FETCH_SIZE"), counter_means(write_dir, "WRITE_SIZE")
+    f_scale = PROBE_BYTES / (fetch["bitwise_not"] * 1024.0)
+    w_scale = PROBE_BYTES / (write["bitwise_not"] * 1024.0)
+    out = {"calibration": {"kernel": "bitwise_not over 256 MiB int32", "fetch_kib": fetch["bitwise_not"],
+                           "write_kib": write["bitwise_not"], "fetch_scale": f_scale, "write_scale": w_scale}}
+    groups = {"qk_lut_kernel": (["qk_lut_kernel"], ["qk_lut.hip", "kvq_device.h"]),
+              "qk_kernel": (["qk_kernel"], ["qk.hip", "kvq_device.h"]),
+              "pv_partial_kernel+pv_combine_kernel": (["pv_partial_kernel", "pv_combine_kernel"],
+                                                      ["pv.hip", "kvq_device.h"])}
+    for name, (kerns, src) in groups.items():
+        if not all(k in fetch and k in write for k in kerns):
+            continue
+        fk, wk = sum(fetch[k] for k in kerns), sum(write[k] for k in kerns)
+        out[name] = {"source_hash": source_hash(src), "fetch_kib": fk, "write_kib": wk,
+                     "hbm_bytes_per_launch": round(fk * 1024.0 * f_scale + wk * 1024.0 * w_scale)}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def cpu_baseline(wl, seed, n_heads, n_layers):
     """Time the oracle (as it stands) on a bounded sample of the same step: the decode-step
-    append and full-length decode attention for n_heads (sequence, kv head) streams of
-    layer 0; report the rate scaled to algorithmic bytes per second."""
-    import numpy as np
+    append and full-length decode attention for n_heads (sequence, kv head) streams of each
+    of n_layers layers; report the rate scaled to algorithmic bytes per second."""
     import torch
     from threadpoolctl import threadpool_limits
+
+    L = wl.seq_len
+    sm = 1.0 / math.sqrt(wl.head_dim)
+    elapsed = 0.0
+    with threadpool_limits(limits=1):
+        torch.set_num_threads(1)
+        for li in range(n_layers):
+            elapsed += cpu_layer(wl, seed + li, n_heads, L, sm)
+    qk, pv, app = algorithmic_bytes(wl, L + 1)
+    per_stream = (qk + pv + app) / (wl.batch * wl.n_kv_heads)
+    return {"value": round(per_stream * n_heads * n_layers / elapsed / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n_heads} of {wl.batch * wl.n_kv_heads} kv-head streams x {n_layers} layers, L={L + 1}: "
+                      f"append of the new token + float64 decode attention, {elapsed:.1f} s, 1 thread"}
+
+
+def cpu_layer(wl, seed, n_heads, L, sm):
+    """Oracle seconds for one layer's sample (the untimed prefix quantization excluded)."""
+    import numpy as np
 
     import oracle
     import synth
 
-    L = wl.seq_len
-    sm = 1.0 / math.sqrt(wl.head_dim)
     ks = synth.key_scale(seed, wl)
     cbk, cbv = synth.codebook(seed, wl.k_bits, "k"), synth.codebook(seed, wl.v_bits, "v")
     q = synth.queries(seed, wl)
     elapsed = 0.0
-    with threadpool_limits(limits=1):
-        torch.set_num_threads(1)
-        for h in range(n_heads):
-            kx = synth.keys(seed, wl, 0, h, L + 1).numpy()
-            vx = synth.values(seed, wl, 0, h, L + 1).numpy()
-            cache = oracle.quantize_stream(kx[:L], vx[:L], ks[h], cbk, cbv, wl.n_outliers)  # prefix: not timed
-            t0 = time.perf_counter()
-            new = oracle.quantize_stream(kx[L:], vx[L:], ks[h], cbk, cbv, wl.n_outliers)
-            full = oracle.StreamCache(*(np.concatenate([a, b]) for a, b in zip(
-                (cache.k_codes, cache.k_idx, cache.k_val, cache.v_codes, cache.v_idx, cache.v_val, cache.v_scale),
-                (new.k_codes, new.k_idx, new.k_val, new.v_codes, new.v_idx, new.v_val, new.v_scale))))
-            oracle.pack_key_records(new.k_codes, wl.k_bits)
-            for hq in range(h * wl.group, (h + 1) * wl.group):
-                oracle.decode_head(q[0, hq].float().numpy().astype(np.float64), full, ks[h], cbk, cbv,
-                                   wl.rope_base, sm)
-            elapsed += time.perf_counter() - t0
-    qk, pv, app = algorithmic_bytes(wl, L + 1)
-    per_stream = (qk + pv + app) / (wl.batch * wl.n_kv_heads)
-    return {"value": round(per_stream * n_heads / elapsed / 1e9, 6), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{n_heads} of {wl.batch * wl.n_kv_heads} kv-head streams of one layer, L={L + 1}: "
-                      f"append of the new token + float64 decode attention, {elapsed:.1f} s, 1 thread"}
+    for h in range(n_heads):
+        kx = synth.keys(seed, wl, 0, h, L + 1).numpy()
+        vx = synth.values(seed, wl, 0, h, L + 1).numpy()
+        cache = oracle.quantize_stream(kx[:L], vx[:L], ks[h], cbk, cbv, wl.n_outliers)  # prefix: not timed
+        t0 = time.perf_counter()
+        new = oracle.quantize_stream(kx[L:], vx[L:], ks[h], cbk, cbv, wl.n_outliers)
+        full = oracle.StreamCache(*(np.concatenate([a, b]) for a, b in zip(
+            (cache.k_codes, cache.k_idx, cache.k_val, cache.v_codes, cache.v_idx, cache.v_val, cache.v_scale),
+            (new.k_codes, new.k_idx, new.k_val, new.v_codes, new.v_idx, new.v_val, new.v_scale))))
+        oracle.pack_key_records(new.k_codes, wl.k_bits)
+        for hq in range(h * wl.group, (h + 1) * wl.group):
+            oracle.decode_head(q[0, hq].float().numpy().astype(np.float64), full, ks[h], cbk, cbv,
+                               wl.rope_base, sm)
+        elapsed += time.perf_counter() - t0
+    return elapsed
 
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
                           "(sharding across GPUs is designed, not built)"}))
@@ -162,22 +225,13 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)
     n_graph_steps = args.warmup + args.steps
 
-    def eager_step(i, kern_events=None):
+    def eager_step(i):
         for lay in layers:
             c = lay["cache"]
             kvq.quantize_append(c, lay["new_k"][i], lay["new_v"][i])
             L = max(c.lengths)
-            if kern_events is not None:
-                e0, e1, e2 = ev(), ev(), ev()
-                e0.record()
             kvq.qk_matvec(c, lay["q"], lay["bufs"].logits, max_len=L)
-            if kern_events is not None:
-                e1.record()
             kvq.pv_matvec(c, lay["bufs"].logits, lay["bufs"].out, lay["bufs"].workspace, max_len=L)
-            if kern_events is not None:
-                e2.record()
-                kern_events["qk"].append((e0, e1))
-                kern_events["pv"].append((e1, e2))
 
     # One HIP graph per decode step: every layer's device-positioned append of that
     # step's new token, then q.K^T and softmax.V over the whole capacity bound (kernels
@@ -222,10 +276,21 @@ def main():
     ms_step = ms_total / args.steps
     assert [int(x) for x in layers[0]["cache"].seq_len.cpu()] == layers[0]["cache"].lengths
 
-    # Per-kernel durations: eager steps with HIP events around each launch (same stream).
+    # Per-launch kernel durations: HIP events (on the launch stream) around the layers'
+    # back-to-back launches of one entry point, so launch overhead overlaps execution.
+    L_now = max(layers[0]["cache"].lengths)
     kern_events = {"qk": [], "pv": []}
-    for i in range(args.kernel_steps):
-        eager_step(n_graph_steps + i, kern_events)
+    for _ in range(args.kernel_steps):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record()
+        for lay in layers:
+            kvq.qk_matvec(lay["cache"], lay["q"], lay["bufs"].logits, max_len=L_now)
+        e1.record()
+        for lay in layers:
+            kvq.pv_matvec(lay["cache"], lay["bufs"].logits, lay["bufs"].out, lay["bufs"].workspace, max_len=L_now)
+        e2.record()
+        kern_events["qk"].append((e0, e1))
+        kern_events["pv"].append((e1, e2))
     torch.cuda.synchronize()
 
     # bytes: lengths grow by n_new per step; use the mean length over the timed steps
@@ -235,14 +300,16 @@ def main():
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     kv_tok_s = args.layers * wl.batch * L_mean / (ms_step * 1e-3)
 
-    kt = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in kern_events.items()}  # ms per launch
-    L_k = start_len + wl.n_new * (args.steps + (args.kernel_steps + 1) / 2.0)
-    qk_bk, pv_bk, _ = algorithmic_bytes(wl, L_k)
+    n_lay = len(layers)
+    kt = {k: sum(a.elapsed_time(b) for a, b in v) / (len(v) * n_lay) for k, v in kern_events.items()}  # ms/launch
+    qk_bk, pv_bk, _ = algorithmic_bytes(wl, L_now)
     dom = max(kt, key=kt.get)
     dom_bytes = {"qk": qk_bk, "pv": pv_bk}[dom]
     achieved = dom_bytes / (kt[dom] * 1e-3) / 1e9
-    src = {"qk": ["qk.hip", "kvq_device.h"], "pv": ["pv.hip", "kvq_device.h"]}[dom]
-    traffic = traffic_from_profile(dom, source_hash(src))
+    qk_name, qk_src = (("qk_lut_kernel", "qk_lut.hip") if wl.group == 1 and wl.k_bits <= 3 else ("qk_kernel", "qk.hip"))
+    dom_name = {"qk": qk_name, "pv": "pv_partial_kernel+pv_combine_kernel"}[dom]
+    src = {"qk": [qk_src, "kvq_device.h"], "pv": ["pv.hip", "kvq_device.h"]}[dom]
+    traffic = traffic_from_profile(dom_name, source_hash(src))
 
     line = {
         "metric": "quantized-KV decode attention: achieved HBM GB/s (% of peak) + KV-tokens/s",
@@ -268,12 +335,19 @@ def main():
                        "pv": round(pv_bk / (kt["pv"] * 1e-3) / 1e9, 1)},
         "graph": bool(args.graph),
         "wall_s_timed": round(wall, 3),
-        "roofline": {"kernel": {"qk": "qk_kernel", "pv": "pv_partial_kernel+pv_combine_kernel"}[dom],
+        "roofline": {"kernel": dom_name, "launches_timed": args.kernel_steps * n_lay,
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
+    if args.traffic_probe:
+        src_p = torch.ones(PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
+        dst_p = torch.empty_like(src_p)
+        torch.bitwise_not(src_p, out=dst_p)
+        torch.cuda.synchronize()
+        del src_p, dst_p
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.seed * 1000, args.cpu_heads)
+        line["cpu_baseline"] = cpu_baseline(wl, args.seed * 1000, min(args.cpu_heads, wl.batch * wl.n_kv_heads),
+                                            args.cpu_layers)
     print(json.dumps(line), flush=True)
 
 

@@ -249,8 +249,10 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   }
 }
 
-// One block per (sequence, query head): 256 threads = 128 channels x 2 halves of the
-// partial list.  Loads are independent, so the loop keeps several in flight.
+// One block per (sequence, query head): 256 threads = 128 channels x 2 halves of the part
+// list.  Each thread loads every (m, l, o[c]) of its parts in one pass (independent loads,
+// up to kCombineRegs parts in registers), so the merge waits for a single round trip.
+constexpr int kCombineRegs = 32;  // parts per half held in registers; more fall back to a second pass
 __global__ __launch_bounds__(256) void pv_combine_kernel(PvArgs a) {
   __shared__ float red[4];
   __shared__ float acc_n[kHeadDim], acc_d[kHeadDim];
@@ -265,8 +267,20 @@ __global__ __launch_bounds__(256) void pv_combine_kernel(PvArgs a) {
   const int n_tiles = (L + kTile - 1) / kTile;
   const int np = min(a.n_parts, (n_tiles + a.tiles_per_block - 1) / a.tiles_per_block);
 
+  float mj[kCombineRegs], lj[kCombineRegs], oj[kCombineRegs];
+#pragma unroll
+  for (int r = 0; r < kCombineRegs; ++r) {
+    const int j = half + 2 * r;
+    const bool ok = j < np;
+    const float* pj = src + static_cast<size_t>(ok ? j : 0) * part_stride;
+    mj[r] = ok ? pj[kHeadDim] : -INFINITY;
+    lj[r] = pj[kHeadDim + 1];
+    oj[r] = pj[c];
+  }
   float M = -INFINITY;
-  for (int j = tid; j < np; j += 256) M = fmaxf(M, src[j * part_stride + kHeadDim]);
+#pragma unroll
+  for (int r = 0; r < kCombineRegs; ++r) M = fmaxf(M, mj[r]);
+  for (int j = half + 2 * kCombineRegs; j < np; j += 2) M = fmaxf(M, src[j * part_stride + kHeadDim]);
   M = wave_max_f32(M);
   if ((tid & 63) == 0) red[tid >> 6] = M;
   __syncthreads();
@@ -274,11 +288,16 @@ __global__ __launch_bounds__(256) void pv_combine_kernel(PvArgs a) {
 
   float num = 0.0f, den = 0.0f;
   if (M > -INFINITY) {
-#pragma unroll 4
-    for (int j = half; j < np; j += 2) {
+#pragma unroll
+    for (int r = 0; r < kCombineRegs; ++r) {
+      const float wj = mj[r] > -INFINITY ? expf(mj[r] - M) : 0.0f;
+      num += wj * oj[r];
+      den += wj * lj[r];
+    }
+    for (int j = half + 2 * kCombineRegs; j < np; j += 2) {
       const float* pj = src + j * part_stride;
-      const float mj = pj[kHeadDim];
-      const float wj = mj > -INFINITY ? expf(mj - M) : 0.0f;
+      const float m = pj[kHeadDim];
+      const float wj = m > -INFINITY ? expf(m - M) : 0.0f;
       num += wj * pj[c];
       den += wj * pj[kHeadDim + 1];
     }
