@@ -47,7 +47,8 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   constexpr int kPairEntries = 1 << (2 * VB);
 
   __shared__ uint32_t lut2[kPairEntries];         // fp16 (cb[a], cb[b]) for a token pair
-  __shared__ float osp[kWaves][G][kHeadDim];      // per-wave outlier corrections
+  __shared__ float osp[kWaves][G][kHeadDim];      // per-wave outlier corrections past the first two
+  __shared__ int osi[kWaves][G][kHeadDim];        // per-wave, per-tile fixed-point outlier sums
   __shared__ float wm[kWaves][G], wl[kWaves][G];  // per-wave max and sum
   __shared__ float wo[kWaves][G][kHeadDim];       // per-wave weighted sums
 
@@ -130,7 +131,10 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   load(w_lo, bufA);  // unconditional, so the compiler counts the loads in flight exactly
 
   lut2[tid & (kPairEntries - 1)] = cb_a | (cb_b << 16);  // threads sharing an entry write the same value
-  for (int e = tid; e < kWaves * G * kHeadDim; e += kThreads) (&osp[0][0][0])[e] = 0.0f;
+  for (int e = tid; e < kWaves * G * kHeadDim; e += kThreads) {
+    (&osp[0][0][0])[e] = 0.0f;
+    (&osi[0][0][0])[e] = 0;
+  }
   const float zc = zero_code_value<kNc>(cb_lo, lane);  // value every outlier slot decodes to
   block_lds_barrier();
 
@@ -167,19 +171,55 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
       wts[h] = pr[h] * s;
     }
     wave_lds_sync();
-    // Outliers: the dense code at an outlier channel is the zero code, so add
-    // p_t * (x_c - zc * s_t) to channel c.
-    auto add_outlier = [&](int c, uint32_t vbits) {
-      c &= kHeadDim - 1;  // a token past the length may hold stale bytes
-      const float dv = half_bits_to_float(vbits) - zc * s;
+    // Outliers: the dense code at an outlier channel is the zero code, so channel c gets
+    // p_t * (x_c - zc * s_t).  Float atomics on LDS are slow on this device (about 190
+    // cycles per wave instruction), so the first two outliers of every token are summed
+    // per tile in 32-bit fixed point with integer atomics: the scale 2^(23 - e), with
+    // 2^e above the tile's largest |contribution|, keeps each term below 2^23 and the sum
+    // of at most 128 terms inside int32, rounding each term to 2^-23 of that maximum.
+    // Each channel lane folds its two channels into its accumulators after the dense part.
+    float unscale = 0.0f;
+    bool have_fixed = false;
+    {
+      const float dv0 = half_bits_to_float(d.ov[0]) - zc * s;
+      const float dv1 = half_bits_to_float(d.ov[1]) - zc * s;
+      const int c0 = d.oi[0] & (kHeadDim - 1), c1 = d.oi[1] & (kHeadDim - 1);  // stale bytes past the length
+      float mloc = 0.0f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) atomicAdd(&my_osp[h * kHeadDim + c], pr[h] * dv);
-    };
-    if (kp >= 1) add_outlier(d.oi[0], d.ov[0]);
-    if (kp >= 2) add_outlier(d.oi[1], d.ov[1]);
-    if (valid) {
+      for (int h = 0; h < G; ++h) mloc = fmaxf(mloc, pr[h] * fmaxf(kp >= 1 ? fabsf(dv0) : 0.0f, kp >= 2 ? fabsf(dv1) : 0.0f));
+      const float m = wave_max_f32(mloc);  // one scale for every head of the group
+      have_fixed = m > 0.0f;               // wave-uniform
+      if (have_fixed) {
+        const int e = min(max(static_cast<int>((__builtin_bit_cast(uint32_t, m) >> 23) & 0xffu) - 126, -100), 100);
+        const float sc = __builtin_bit_cast(float, static_cast<uint32_t>(23 - e + 127) << 23);  // 2^(23-e)
+        unscale = __builtin_bit_cast(float, static_cast<uint32_t>(e - 23 + 127) << 23);       // 2^(e-23)
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          int* row = &osi[wave][h][0];
+          if (kp >= 1) atomicAdd(row + c0, static_cast<int>(rintf(pr[h] * dv0 * sc)));
+          if (kp >= 2) atomicAdd(row + c1, static_cast<int>(rintf(pr[h] * dv1 * sc)));
+        }
+      }
+    }
+    if (k > kPrefetchOutliers && valid) {
       const size_t slot = stream * S + t;
-      for (int j = kPrefetchOutliers; j < k; ++j) add_outlier(a.v_idx[slot * k + j], a.v_val[slot * k + j]);
+      for (int j = kPrefetchOutliers; j < k; ++j) {
+        const int c = a.v_idx[slot * k + j] & (kHeadDim - 1);
+        const float dv = half_bits_to_float(a.v_val[slot * k + j]) - zc * s;
+#pragma unroll
+        for (int h = 0; h < G; ++h) atomicAdd(&my_osp[h * kHeadDim + c], pr[h] * dv);
+      }
+    }
+    wave_lds_sync();
+    if (have_fixed) {  // this tile's fixed-point outlier sums of channels (2l, 2l+1), then clear them
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        int2* cell = reinterpret_cast<int2*>(&osi[wave][h][2 * lane]);
+        const int2 q = *cell;
+        acc[h][0] = fmaf(static_cast<float>(q.x), unscale, acc[h][0]);
+        acc[h][1] = fmaf(static_cast<float>(q.y), unscale, acc[h][1]);
+        *cell = make_int2(0, 0);
+      }
     }
     // Dense part: lane = channel pair; the token weights come from lane t as scalars.
     float accp[G][2][2];
@@ -204,6 +244,7 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
       acc[h][0] += accp[h][0][0] + accp[h][0][1];
       acc[h][1] += accp[h][1][0] + accp[h][1][1];
     }
+    wave_lds_sync();  // the cleared cells are written before the next tile's atomics
   };
 
   if (w_lo < w_hi) {
