@@ -110,6 +110,23 @@ __device__ __forceinline__ uint32_t nearest_code(float u, const float* cb) {
 
 // Index of the codebook entry nearest to 0 (the code of every dense-zero entry, in
 // particular of every outlier slot): smallest j minimising |0 - cb[j]|.
+// Small lookup tables indexed by per-lane codes are read with random indices, and bank
+// conflicts make such reads several times slower than conflict-free ones.  The table is
+// therefore stored in kCopies interleaved copies: entry e of copy r at word e * kCopies + r,
+// lane l reading copy l % kCopies, so every lane reads its own bank.  Tables of more than 64
+// entries stay single (a 256-entry table would take 64 KB).
+template <int ENTRIES>
+struct RepTable {
+  static constexpr int kCopies = ENTRIES <= 64 ? 64 : 1;
+  static constexpr int kWords = ENTRIES * kCopies;
+  // byte offset of this lane's copy of entry 0
+  __device__ static __forceinline__ uint32_t lane_base(int lane) {
+    return kCopies > 1 ? static_cast<uint32_t>(lane & (kCopies - 1)) * 4u : 0u;
+  }
+  // byte offset of entry e for a lane whose lane_base is `base`
+  __device__ static __forceinline__ uint32_t at(uint32_t e, uint32_t base) { return e * (4u * kCopies) + base; }
+};
+
 // Block barrier for data exchanged through LDS only.  It waits for this wave's LDS
 // operations and then for every wave of the block, but not for outstanding global loads
 // (a workgroup-scope fence, as in __syncthreads, drains those too), so prefetched tiles

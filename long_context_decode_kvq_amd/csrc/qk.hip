@@ -79,7 +79,8 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   constexpr bool kFoldScale = G == 1;
 
   __shared__ float2 et[kHalf][kTile];       // R(tau) for pair i: (cos, sin) of tau * theta_i
-  __shared__ uint32_t lutp[kPairEntries];   // fp16 (cb[a], cb[b]) for a pair field a | b << KB
+  using Tab = RepTable<kPairEntries>;
+  __shared__ uint32_t lutp[Tab::kWords];    // fp16 (cb[a], cb[b]) for a pair field a | b << KB, replicated
   __shared__ float ks[kHeadDim];
   __shared__ float2 ksp[kHalf];             // (s_i, s_{i+64})
   __shared__ float2 qr[kWaves][G][kHalf];   // per-wave tile-rotated query pairs
@@ -169,8 +170,6 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   const float ks_hi = a.k_scale[kvh * kHeadDim + (tid & (kHalf - 1)) + kHalf];
   const uint32_t cb_lo = a.k_cb[lane & (kNc - 1)];
   static_assert(kPairEntries <= 256, "one table entry per thread");
-  const uint32_t cb_pa = a.k_cb[tid & (kNc - 1)];
-  const uint32_t cb_pb = a.k_cb[(tid >> KB) & (kNc - 1)];
   const double th_rev = a.theta_rev[lane];
 
   // The first two tiles are requested before the tables are built, so their memory
@@ -184,7 +183,12 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   // ---- per-block tables -----------------------------------------------------------
   ks[tid & (kHeadDim - 1)] = ks_own;
   ksp[tid & (kHalf - 1)] = make_float2(ks_lo, ks_hi);
-  lutp[tid & (kPairEntries - 1)] = cb_pa | (cb_pb << 16);
+  for (int wd = tid; wd < Tab::kWords; wd += 256) {  // word wd holds entry wd / copies
+    const int e = wd / Tab::kCopies;                 // codebook entries from the lanes holding them
+    const uint32_t lo = static_cast<uint32_t>(__shfl(static_cast<int>(cb_lo), e & (kNc - 1))) & 0xffffu;
+    const uint32_t hi = static_cast<uint32_t>(__shfl(static_cast<int>(cb_lo), e >> KB)) & 0xffffu;
+    lutp[wd] = lo | (hi << 16);
+  }
   float qa[kSlots][G], qb[kSlots][G];
 #pragma unroll
   for (int j = 0; j < kSlots; ++j)
@@ -245,6 +249,7 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   if (n_tiles <= 0) return;  // after the block's last barrier
 
   const int my_slot = lane >> 4;
+  const uint32_t tab_base = Tab::lane_base(lane);
   static_assert(kSlots == 4, "four 16-lane rows");
   auto pick = [&](float v0, float v1, float v2, float v3) {
     return my_slot == 0 ? v0 : my_slot == 1 ? v1 : my_slot == 2 ? v2 : v3;
@@ -298,7 +303,8 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
 
     static_for<0, kHalf>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      const uint32_t e2 = lutp[field<2 * KB, 2 * KB * i>(d.w)];
+      const uint32_t e2 = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(lutp) +
+                                                            Tab::at(field<2 * KB, 2 * KB * i>(d.w), tab_base));
       float cr, ci;
       if constexpr (i < kRegPairs) {
         cr = er[i];

@@ -35,7 +35,7 @@ template <int KB>
 struct LutShape {
   static constexpr int kNc = 1 << KB;
   static constexpr int kNe = kNc * kNc;               // code pairs (a | b << KB) per rotary pair
-  static constexpr int kBufs = KB == 4 ? 1 : 2;       // 4-bit tables take 128 KB: single buffer
+  static constexpr int kBufs = 2;                     // double-buffered (2- and 3-bit codes only)
   static constexpr int kBufBytes = kHalf * kNe * 8;   // 64 rows of (A, B) float pairs
 };
 
@@ -142,11 +142,11 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   for (int j = 0; j < 2; ++j) qv[j] = a.q_is_fp16 ? half_bits_to_float(qraw[j]) : __builtin_bit_cast(float, qraw[j]);
   const float zc = zero_code_value<kNc>(cb_lane, lane);  // value every outlier slot decodes to
   // codebook values this lane's table entries use: entry e = a | b << KB
-  float cba[4], cbb;
+  float cba[1], cbb;
   {
-    const int e0 = KB == 4 ? 4 * lane : (KB == 3 ? lane : (lane & 15));
+    const int e0 = KB == 3 ? lane : (lane & 15);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cba[j] = half_bits_to_float(__shfl(static_cast<int>(cb_lane), (e0 + j) & (kNc - 1)) & 0xffffu);
+    for (int j = 0; j < 1; ++j) cba[j] = half_bits_to_float(__shfl(static_cast<int>(cb_lane), (e0 + j) & (kNc - 1)) & 0xffffu);
     cbb = half_bits_to_float(__shfl(static_cast<int>(cb_lane), (e0 >> KB) & (kNc - 1)) & 0xffffu);
   }
 
@@ -179,20 +179,15 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
     float2 p1;
     coef(th_P, qv[0], qv[1], sP_lo, sP_hi, c1, p1);
     if (lane < 8) pab[b * kHalf + P] = p1;
-    if constexpr (KB >= 3) {
+    static_assert(KB == 2 || KB == 3, "2- and 3-bit keys");
+    if constexpr (KB == 3) {
       // wave w fills the rows of pairs w + 8 m, m < 8; lane m holds their coefficients
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int i = wave + kLutWaves * m;
         const float al = lane_f32(c1.x, m), be = lane_f32(c1.y, m), ga = lane_f32(c1.z, m), nd = lane_f32(c1.w, m);
         const float gb = ga * cbb, db = nd * cbb;
-        if constexpr (KB == 3) {
-          T[i * kNe + lane] = make_float2(fmaf(al, cba[0], gb), fmaf(be, cba[0], db));
-        } else {
-          float4* row = reinterpret_cast<float4*>(T + i * kNe + 4 * lane);
-          row[0] = make_float4(fmaf(al, cba[0], gb), fmaf(be, cba[0], db), fmaf(al, cba[1], gb), fmaf(be, cba[1], db));
-          row[1] = make_float4(fmaf(al, cba[2], gb), fmaf(be, cba[2], db), fmaf(al, cba[3], gb), fmaf(be, cba[3], db));
-        }
+        T[i * kNe + lane] = make_float2(fmaf(al, cba[0], gb), fmaf(be, cba[0], db));
       }
     } else {
       // 16 entries per row: one fill step covers the rows of 4 pairs, m = 4 f + (lane >> 4),
@@ -272,20 +267,11 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   build(s_lo, 0);
   block_lds_barrier();
   auto step = [&](int s, LutRec<KB>& cur, LutRec<KB>& next2) {
-    const int b = Sh::kBufs == 2 ? ((s - s_lo) & 1) : 0;
+    const int b = (s - s_lo) & 1;
     load_rec(s + 2, next2);
-    if constexpr (Sh::kBufs == 2) {
-      if (s + 1 < s_hi) build(s + 1, b ^ 1);
-      compute(s, b, cur);
-      block_lds_barrier();
-    } else {
-      compute(s, 0, cur);
-      block_lds_barrier();
-      if (s + 1 < s_hi) {
-        build(s + 1, 0);
-        block_lds_barrier();
-      }
-    }
+    if (s + 1 < s_hi) build(s + 1, b ^ 1);
+    compute(s, b, cur);
+    block_lds_barrier();
   };
   for (int s = s_lo; s < s_hi; s += 3) {
     step(s, r0, r2);
@@ -330,7 +316,6 @@ hipError_t launch_qk_lut_t(int batch, const QkArgs& a0, hipStream_t st) {
 hipError_t launch_qk_lut(int k_bits, int batch, const QkArgs& a, hipStream_t s) {
   if (k_bits == 2) return launch_qk_lut_t<2>(batch, a, s);
   if (k_bits == 3) return launch_qk_lut_t<3>(batch, a, s);
-  if (k_bits == 4) return launch_qk_lut_t<4>(batch, a, s);
   return hipErrorInvalidValue;
 }
 
