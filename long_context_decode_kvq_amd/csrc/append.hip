@@ -9,7 +9,9 @@
 // the step touches (device positions).  Inside a wave a vector's 128 channels sit two per
 // lane: keys as (l, l + 64) -- the two halves of rotary pair l, adjacent in the key
 // record -- and values as (2l, 2l + 1), which is how the value tile stores them.  Each
-// value tile has exactly one writer wave, so its read-modify-write needs no atomics.
+// value tile has exactly one writer wave per call: a bulk append copies the tile through
+// LDS and writes it back; a decode step's few tokens instead clear and set their code
+// fields in place with global and/or atomics, which saves the dependent read of the tile.
 //
 // Device positions: each block reads its sequence's start from seq_len with an atomic
 // that also counts the block's arrival in the word's high bits; the last block to arrive
@@ -45,6 +47,8 @@ __device__ __forceinline__ void select_outliers(uint32_t key0, uint32_t key1, in
   }
 }
 
+constexpr int kInPlaceTokens = 4;  // new tokens per tile written with atomics instead of a tile copy
+
 template <int KB, int VB>
 __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
   constexpr int kNcK = 1 << KB;
@@ -69,6 +73,25 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
   const int S = a.max_seq;
   const int k = a.n_outliers;
 
+  // The block's first new token is known before its position is: token 0 with device
+  // positions (one block per sequence and head), else the first token of this block's tile.
+  // Its input vectors and the key scales are requested before the position atomic's
+  // round trip, so the two latencies overlap.
+  const int j_first = a.device_positions ? 0 : max(0, (a.start[seq] / kTile + static_cast<int>(blockIdx.x)) * kTile - a.start[seq]);
+  const size_t src_first = ((static_cast<size_t>(seq) * a.n_max + min(j_first, max(a.n_max - 1, 0))) * H + kvh) * kHeadDim;
+  const bool have_first = j_first < count && a.n_max > 0;
+  uint32_t pre0 = 0u, pre1 = 0u;
+  if (have_first) {
+    if (is_key_wave) {
+      pre0 = a.k_new[src_first + lane];
+      pre1 = a.k_new[src_first + lane + kHalf];
+    } else {
+      pre0 = reinterpret_cast<const uint32_t*>(a.v_new + src_first)[lane];
+    }
+  }
+  const float ks0 = a.k_scale[kvh * kHeadDim + lane];
+  const float ks1 = a.k_scale[kvh * kHeadDim + lane + kHalf];
+
   if (tid == 0) {
     if (a.device_positions) {
       const int nblk = gridDim.x * gridDim.y;
@@ -90,8 +113,6 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
 
   const size_t stream = static_cast<size_t>(seq) * H + kvh;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const float ks0 = a.k_scale[kvh * kHeadDim + lane];
-  const float ks1 = a.k_scale[kvh * kHeadDim + lane + kHalf];
   const int first_tile = start / kTile;
   const int last_tile = (start + count - 1) / kTile;
 
@@ -99,7 +120,10 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
     const int lo = max(start, tile * kTile);
     const int hi = min(start + count, (tile + 1) * kTile);
     uint32_t* vtile = reinterpret_cast<uint32_t*>(a.v_codes + (stream * (S / kTile) + tile) * (1024 * VB));
-    if (!is_key_wave) {
+    // A few tokens update their code fields in place with global atomics (disjoint bits of
+    // shared words), so the tile is never read; more read-modify-write it through LDS.
+    const bool in_place = hi - lo <= kInPlaceTokens;
+    if (!is_key_wave && !in_place) {
       for (int i = lane; i < kWave * kLaneWords; i += kWave) vt[i] = vtile[i];
       wave_lds_sync();
     }
@@ -107,10 +131,11 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
       const int j = t - start;  // row of this token in the new-token block
       const size_t src = ((static_cast<size_t>(seq) * a.n_max + j) * H + kvh) * kHeadDim;
       const size_t slot = stream * S + t;
+      const bool use_pre = j == j_first && have_first;
       if (is_key_wave) {
         // ---- key: channels (lane, lane + 64), per-channel scale ----------------------
-        const uint32_t x0 = a.k_new[src + lane];
-        const uint32_t x1 = a.k_new[src + lane + kHalf];
+        const uint32_t x0 = use_pre ? pre0 : a.k_new[src + lane];
+        const uint32_t x1 = use_pre ? pre1 : a.k_new[src + lane + kHalf];
         bool sel0, sel1;
         select_outliers(outlier_key(x0, lane), outlier_key(x1, lane + kHalf), k, sel0, sel1);
         const uint64_t b0 = __ballot(sel0);
@@ -142,7 +167,7 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
         wave_lds_sync();
       } else {
         // ---- value: channels (2 lane, 2 lane + 1), one scale per vector --------------
-        const uint32_t xx = reinterpret_cast<const uint32_t*>(a.v_new + src)[lane];
+        const uint32_t xx = use_pre ? pre0 : reinterpret_cast<const uint32_t*>(a.v_new + src)[lane];
         const uint32_t x0 = xx & 0xffffu;
         const uint32_t x1 = xx >> 16;
         bool sel0, sel1;
@@ -174,17 +199,26 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
         const int w = bit >> 5;
         const int sh = bit & 31;
         constexpr uint32_t mask = (1u << VB) - 1u;
-        uint32_t* seg = vt + lane * kLaneWords;
+        uint32_t* seg = (in_place ? vtile : vt) + lane * kLaneWords;
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
           const uint32_t code = ch ? c1 : c0;
           uint32_t* cw = seg + ch * kChanWords;
-          cw[w] = (cw[w] & ~(mask << sh)) | (code << sh);
-          if (sh + VB > 32) cw[w + 1] = (cw[w + 1] & ~(mask >> (32 - sh))) | (code >> (32 - sh));
+          if (in_place) {
+            atomicAnd(cw + w, ~(mask << sh));
+            atomicOr(cw + w, code << sh);
+            if (sh + VB > 32) {
+              atomicAnd(cw + w + 1, ~(mask >> (32 - sh)));
+              atomicOr(cw + w + 1, code >> (32 - sh));
+            }
+          } else {
+            cw[w] = (cw[w] & ~(mask << sh)) | (code << sh);
+            if (sh + VB > 32) cw[w + 1] = (cw[w + 1] & ~(mask >> (32 - sh))) | (code >> (32 - sh));
+          }
         }
       }
     }
-    if (!is_key_wave) {
+    if (!is_key_wave && !in_place) {
       wave_lds_sync();
       for (int i = lane; i < kWave * kLaneWords; i += kWave) vtile[i] = vt[i];
       wave_lds_sync();
