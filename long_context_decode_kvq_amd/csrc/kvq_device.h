@@ -82,6 +82,28 @@ __device__ __forceinline__ uint32_t field(const uint32_t (&w)[N]) {
   }
 }
 
+// base + (field<BITS, POS>(w) << SHIFT): the LDS byte address of entry `field` of a table
+// of (1 << SHIFT)-byte entries at `base` (wave-uniform).  Written as a bit-field extract
+// and a shift-add: the compiler otherwise forms a shift, a mask and an add.
+template <int BITS, int POS, int SHIFT, int N>
+__device__ __forceinline__ uint32_t field_addr(const uint32_t (&w)[N], uint32_t base) {
+  constexpr int wi = POS / 32;
+  constexpr int sh = POS % 32;
+  static_assert(wi < N, "field outside the word array");
+  uint32_t r;
+  if constexpr (sh + BITS <= 32) {
+    asm("v_bfe_u32 %0, %1, %2, %3\n\tv_lshl_add_u32 %0, %0, %4, %5"
+        : "=&v"(r)
+        : "v"(w[wi]), "n"(sh), "n"(BITS), "n"(SHIFT), "s"(base));
+  } else {
+    static_assert(wi + 1 < N, "straddling field outside the word array");
+    asm("v_alignbit_b32 %0, %1, %2, %3\n\tv_bfe_u32 %0, %0, 0, %4\n\tv_lshl_add_u32 %0, %0, %5, %6"
+        : "=&v"(r)
+        : "v"(w[wi + 1]), "v"(w[wi]), "n"(sh), "n"(BITS), "n"(SHIFT), "s"(base));
+  }
+  return r;
+}
+
 // Compile-time loop: calls f(std::integral_constant<int, I>) for I in [0, N).
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -147,6 +169,11 @@ __device__ __forceinline__ float zero_code_value(uint32_t cb_bits, int lane) {
   const uint32_t key = lane < NC ? ((cb_bits & 0x7fffu) << 8) | static_cast<uint32_t>(lane) : 0xffffffffu;
   const uint32_t m = ~wave_max_u32(~key);  // wave minimum
   return half_bits_to_float(static_cast<uint32_t>(__shfl(static_cast<int>(cb_bits), static_cast<int>(m & 0xffu))) & 0xffffu);
+}
+
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
 }
 
 // cos/sin of 2*pi*r for a revolution count r already reduced to [0, 1).

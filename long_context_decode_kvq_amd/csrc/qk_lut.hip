@@ -205,7 +205,8 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
 
   // ---- one tile of super-tile s from buffer b ------------------------------------------
   auto compute = [&](int s, int b, const LutRec<KB>& d) {
-    const float2* T = lut + b * (Sh::kBufBytes / 8);
+    const uint32_t T = lds_address(lut + b * (Sh::kBufBytes / 8));
+    const unsigned char* lb = lds - lds_address(lds);  // LDS address -> pointer
     // Software-pipelined over batches of kBatch pairs: the table reads of batch j + 1 are
     // issued before the FMAs of batch j, so each read's latency is covered by a batch of
     // arithmetic (the scheduling barriers keep the compiler from re-serializing them).
@@ -217,8 +218,7 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
       static_for<0, kBatch>([&](auto uc) {
         constexpr int u = decltype(uc)::value;
         constexpr int i = j * kBatch + u;
-        const uint32_t e = field<2 * KB, 2 * KB * i>(d.w);
-        const float2 v = T[i * kNe + e];
+        const float2 v = *reinterpret_cast<const float2*>(lb + field_addr<2 * KB, 2 * KB * i, 3>(d.w, T) + i * kNe * 8);
         va[j & 1][u] = v.x;
         vb[j & 1][u] = v.y;
       });
