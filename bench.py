@@ -33,6 +33,8 @@ def parse():
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-fp16-baseline", dest="fp16_baseline", action="store_false",
+                   help="skip timing the uncompressed fp16 kernels at the same shape")
     p.add_argument("--cpu-heads", type=int, default=32, help="kv-head streams per layer the oracle times in the CPU leg")
     p.add_argument("--cpu-layers", type=int, default=4, help="layers the oracle times in the CPU leg")
     p.add_argument("--kernel-steps", type=int, default=5,
@@ -175,6 +177,50 @@ def cpu_layer(wl, seed, n_heads, L, sm):
                                wl.rope_base, sm)
         elapsed += time.perf_counter() - t0
     return elapsed
+
+
+def fp16_baseline(wl, cfg, L, kernel_steps, kt, n_layers=4):
+    """The uncompressed fp16 kernels on the same shape: seeded fp16 caches of n_layers layers
+    (each larger than the 256 MB last-level cache), per-launch times measured like the
+    compressed kernels', and the compressed path's speed-up over them."""
+    import torch
+
+    import long_context_decode_kvq_amd as kvq
+    import synth
+    gen = torch.Generator(device="cuda").manual_seed(12345)
+    caches = []
+    for li in range(n_layers):
+        c = kvq.Fp16Cache(cfg)
+        c.k.copy_(torch.randn(c.k.shape, generator=gen, device="cuda").half())
+        c.v.copy_(torch.randn(c.v.shape, generator=gen, device="cuda").half())
+        c.set_lengths([L] * cfg.batch)
+        caches.append((c, synth.queries(li, wl, "cuda"), kvq.DecodeBuffers(c)))
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    rounds = {"qk": [], "pv": []}
+    for _ in range(kernel_steps + 1):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record()
+        for c, q, b in caches:
+            kvq.fp16_qk_matvec(c, q, b.logits, max_len=L)
+        e1.record()
+        for c, q, b in caches:
+            kvq.fp16_pv_matvec(c, b.logits, b.out, b.workspace, max_len=L)
+        e2.record()
+        rounds["qk"].append((e0, e1))
+        rounds["pv"].append((e1, e2))
+    torch.cuda.synchronize()
+    ms = {k: sum(a.elapsed_time(b) for a, b in v[1:]) / (kernel_steps * n_layers) for k, v in rounds.items()}
+    per_head_tok = cfg.batch * cfg.n_kv_heads * L
+    byt = {"qk": per_head_tok * 256 + 4 * cfg.batch * cfg.n_q_heads * L,
+           "pv": per_head_tok * 256 + 4 * cfg.batch * cfg.n_q_heads * L}
+    del caches
+    torch.cuda.empty_cache()
+    return {"kernel_ms": {k: round(v, 5) for k, v in ms.items()},
+            "kernel_gbs": {k: round(byt[k] / (ms[k] * 1e-3) / 1e9, 1) for k in ms},
+            "speedup_of_quantized": {"qk": round(ms["qk"] / kt["qk"], 3), "pv": round(ms["pv"] / kt["pv"], 3),
+                                     "qk+pv": round((ms["qk"] + ms["pv"]) / (kt["qk"] + kt["pv"]), 3)},
+            "layers_timed": n_layers, "data": "seeded N(0,1) fp16 keys (as stored after RoPE) and values"}
 
 
 def main():
@@ -339,6 +385,8 @@ def main():
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
+    if args.fp16_baseline:
+        line["fp16_baseline"] = fp16_baseline(wl, cfg, L_now, args.kernel_steps, kt)
     if args.traffic_probe:
         src_p = torch.ones(PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
         dst_p = torch.empty_like(src_p)

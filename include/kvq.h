@@ -156,6 +156,26 @@ int kvq_qk_matvec(const kvq_shape* shape, const kvq_cache* cache, const void* q,
 int kvq_pv_matvec(const kvq_shape* shape, const kvq_cache* cache, const float* logits, float* out,
                   void* workspace, size_t workspace_bytes, int32_t max_len, hipStream_t stream);
 
+/*
+ * Uncompressed fp16 decode attention over a plain fp16 cache: the comparison point the
+ * pages quote the compressed kernels against (summary page, abstract paragraph: custom
+ * kernels faster than fp16 matrix-vector products).  Same logits and outputs as
+ * kvq_qk_matvec / kvq_pv_matvec, over
+ *   k_fp16, v_fp16  fp16 bits [B][Hkv][max_seq][D], token-major; the keys already rotated
+ *                   at their own positions (an fp16 cache stores keys after RoPE), so
+ *                   logits[b][h][t] = sm_scale * q[b][h] . k_fp16[b][h/g][t].
+ *   seq_len         device int32 [B], tokens held per sequence (low 24 bits).
+ * Only batch, n_q_heads, n_kv_heads, head_dim and max_seq of `shape` are used (and
+ * checked: head_dim 128, max_seq a multiple of 64, group in {1, 2, 4, 8}).  The fp16 pv
+ * workspace is sized like the compressed one: kvq_workspace_bytes of a valid shape with
+ * the same heads and max_seq.  Errors and asynchrony as for the compressed calls.
+ */
+int kvq_fp16_qk_matvec(const kvq_shape* shape, const uint16_t* k_fp16, const int32_t* seq_len, const void* q,
+                       int32_t q_is_fp16, float sm_scale, float* logits, int32_t max_len, hipStream_t stream);
+int kvq_fp16_pv_matvec(const kvq_shape* shape, const uint16_t* v_fp16, const int32_t* seq_len,
+                       const float* logits, float* out, void* workspace, size_t workspace_bytes,
+                       int32_t max_len, hipStream_t stream);
+
 /* Human-readable name of a kvq_status value (static string). */
 const char* kvq_status_string(int status);
 

@@ -22,7 +22,8 @@ KVQ_OK = 0
 STATUS_NAMES = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID", -2: "KVQ_ERR_UNSUPPORTED",
                 -3: "KVQ_ERR_CAPACITY", -4: "KVQ_ERR_WORKSPACE", -5: "KVQ_ERR_HIP"}
 EXPORTED = ("kvq_cache_sizes", "kvq_workspace_bytes", "kvq_quantize_append", "kvq_qk_matvec",
-            "kvq_pv_matvec", "kvq_status_string", "kvq_abi_version")
+            "kvq_pv_matvec", "kvq_fp16_qk_matvec", "kvq_fp16_pv_matvec", "kvq_status_string",
+            "kvq_abi_version")
 ABI_VERSION = 1
 
 
@@ -77,6 +78,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_pv_matvec.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(CacheDesc), P, P, P, SZ,
                                   I32, P]
     lib.kvq_pv_matvec.restype = ctypes.c_int
+    lib.kvq_fp16_qk_matvec.argtypes = [ctypes.POINTER(Shape), P, P, P, I32, ctypes.c_float, P, I32, P]
+    lib.kvq_fp16_qk_matvec.restype = ctypes.c_int
+    lib.kvq_fp16_pv_matvec.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, SZ, I32, P]
+    lib.kvq_fp16_pv_matvec.restype = ctypes.c_int
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_abi_version.argtypes = []
@@ -259,4 +264,64 @@ def decode_attention(cache: KVCache, q: torch.Tensor, bufs: DecodeBuffers, sm_sc
     """q.K^T then softmax.V over the compressed cache; returns bufs.out [B][Hq][D]."""
     qk_matvec(cache, q, bufs.logits, sm_scale, max_len, stream)
     pv_matvec(cache, bufs.logits, bufs.out, bufs.workspace, max_len, stream)
+    return bufs.out
+
+
+class Fp16Cache:
+    """A plain fp16 KV cache (the baseline the compressed kernels are compared with):
+    k, v fp16 [B][Hkv][max_seq][D], keys stored after the rotary embedding, and the device
+    lengths seq_len int32 [B]."""
+
+    def __init__(self, cfg: CacheConfig, device="cuda"):
+        self.cfg = cfg
+        shape = (cfg.batch, cfg.n_kv_heads, cfg.max_seq, cfg.head_dim)
+        self.k = torch.zeros(shape, dtype=torch.float16, device=device)
+        self.v = torch.zeros(shape, dtype=torch.float16, device=device)
+        self.seq_len = torch.zeros(cfg.batch, dtype=torch.int32, device=device)
+        self.lengths = [0] * cfg.batch
+        self._shape = cfg.shape()
+
+    def set_lengths(self, lengths):
+        self.lengths = [int(x) for x in lengths]
+        self.seq_len.copy_(torch.tensor(self.lengths, dtype=torch.int32))
+
+    @property
+    def nbytes(self) -> int:
+        return self.k.numel() * 2 + self.v.numel() * 2
+
+
+def fp16_qk_matvec(cache: Fp16Cache, q: torch.Tensor, logits: torch.Tensor, sm_scale: float | None = None,
+                   max_len: int | None = None, stream=None):
+    """kvq_fp16_qk_matvec: q [B][Hq][D] fp32/fp16 -> logits fp32 [B][Hq][max_seq]."""
+    cfg = cache.cfg
+    assert q.shape == (cfg.batch, cfg.n_q_heads, cfg.head_dim) and q.is_contiguous()
+    assert q.dtype in (torch.float32, torch.float16)
+    assert logits.dtype == torch.float32 and logits.is_contiguous()
+    assert logits.numel() == cfg.batch * cfg.n_q_heads * cfg.max_seq
+    sm = 1.0 / math.sqrt(cfg.head_dim) if sm_scale is None else float(sm_scale)
+    ml = max(max(cache.lengths), 1) if max_len is None else int(max_len)
+    st = load_library().kvq_fp16_qk_matvec(ctypes.byref(cache._shape), cache.k.data_ptr(), cache.seq_len.data_ptr(),
+                                           q.data_ptr(), 1 if q.dtype == torch.float16 else 0, sm,
+                                           logits.data_ptr(), ml, _stream(stream))
+    _check("kvq_fp16_qk_matvec", st)
+
+
+def fp16_pv_matvec(cache: Fp16Cache, logits: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                   max_len: int | None = None, stream=None):
+    """kvq_fp16_pv_matvec: logits fp32 [B][Hq][max_seq] -> out fp32 [B][Hq][D]."""
+    cfg = cache.cfg
+    assert out.dtype == torch.float32 and out.numel() == cfg.batch * cfg.n_q_heads * cfg.head_dim
+    assert logits.dtype == torch.float32 and out.is_contiguous() and workspace.is_contiguous()
+    ml = max(max(cache.lengths), 1) if max_len is None else int(max_len)
+    st = load_library().kvq_fp16_pv_matvec(ctypes.byref(cache._shape), cache.v.data_ptr(), cache.seq_len.data_ptr(),
+                                           logits.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                                           workspace.numel() * workspace.element_size(), ml, _stream(stream))
+    _check("kvq_fp16_pv_matvec", st)
+
+
+def fp16_decode_attention(cache: Fp16Cache, q: torch.Tensor, bufs: DecodeBuffers, sm_scale=None, max_len=None,
+                          stream=None) -> torch.Tensor:
+    """q.K^T then softmax.V over the fp16 cache; returns bufs.out [B][Hq][D]."""
+    fp16_qk_matvec(cache, q, bufs.logits, sm_scale, max_len, stream)
+    fp16_pv_matvec(cache, bufs.logits, bufs.out, bufs.workspace, max_len, stream)
     return bufs.out

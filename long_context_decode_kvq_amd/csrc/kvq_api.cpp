@@ -232,4 +232,60 @@ int kvq_pv_matvec(const kvq_shape* s, const kvq_cache* c, const float* logits, f
   return hip_status(kvq::launch_pv(s->v_bits, s->n_q_heads / s->n_kv_heads, s->batch, a, stream));
 }
 
+// ---- uncompressed fp16 baseline --------------------------------------------------------
+
+static int check_fp16_shape(const kvq_shape* s) {
+  if (!s) return KVQ_ERR_INVALID;
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1 || s->max_seq < 1) return KVQ_ERR_INVALID;
+  if (s->max_seq % kvq::kTile != 0 || s->max_seq > kvq::kMaxSeqLimit) return KVQ_ERR_INVALID;
+  if (s->n_q_heads % s->n_kv_heads != 0) return KVQ_ERR_INVALID;
+  if (s->head_dim != kvq::kHeadDim) return KVQ_ERR_UNSUPPORTED;
+  if (!group_ok(s->n_q_heads / s->n_kv_heads)) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+int kvq_fp16_qk_matvec(const kvq_shape* s, const uint16_t* k_fp16, const int32_t* seq_len, const void* q,
+                       int32_t q_is_fp16, float sm_scale, float* logits, int32_t max_len, hipStream_t stream) {
+  int st = check_fp16_shape(s);
+  if (st != KVQ_OK) return st;
+  if (!k_fp16 || !seq_len || !q || !logits) return KVQ_ERR_INVALID;
+  if (q_is_fp16 != 0 && q_is_fp16 != 1) return KVQ_ERR_INVALID;
+  if (max_len < 1 || max_len > s->max_seq || !std::isfinite(sm_scale)) return KVQ_ERR_INVALID;
+  kvq::Fp16Args a;
+  std::memset(&a, 0, sizeof(a));
+  a.n_q_heads = s->n_q_heads;
+  a.n_kv_heads = s->n_kv_heads;
+  a.max_seq = s->max_seq;
+  a.max_len = max_len;
+  a.q_is_fp16 = q_is_fp16;
+  a.sm_scale = sm_scale;
+  a.q = q;
+  a.k = k_fp16;
+  a.seq_len = seq_len;
+  a.logits = logits;
+  return hip_status(kvq::launch_fp16_qk(s->n_q_heads / s->n_kv_heads, s->batch, a, stream));
+}
+
+int kvq_fp16_pv_matvec(const kvq_shape* s, const uint16_t* v_fp16, const int32_t* seq_len, const float* logits,
+                       float* out, void* workspace, size_t workspace_bytes, int32_t max_len, hipStream_t stream) {
+  int st = check_fp16_shape(s);
+  if (st != KVQ_OK) return st;
+  if (!v_fp16 || !seq_len || !logits || !out) return KVQ_ERR_INVALID;
+  if (max_len < 1 || max_len > s->max_seq) return KVQ_ERR_INVALID;
+  const size_t need = static_cast<size_t>(s->batch) * s->n_q_heads * n_chunks_for(max_len) * (kvq::kHeadDim + 2) * sizeof(float);
+  if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+  kvq::Fp16Args a;
+  std::memset(&a, 0, sizeof(a));
+  a.n_q_heads = s->n_q_heads;
+  a.n_kv_heads = s->n_kv_heads;
+  a.max_seq = s->max_seq;
+  a.max_len = max_len;
+  a.v = v_fp16;
+  a.seq_len = seq_len;
+  a.logits = const_cast<float*>(logits);
+  a.partial = static_cast<float*>(workspace);
+  a.out = out;
+  return hip_status(kvq::launch_fp16_pv(s->n_q_heads / s->n_kv_heads, s->batch, a, stream));
+}
+
 }  // extern "C"

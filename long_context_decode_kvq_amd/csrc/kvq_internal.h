@@ -63,6 +63,20 @@ struct PvArgs {
   float* out;      // [B][Hq][D]
 };
 
+struct Fp16Args {
+  int32_t n_q_heads, n_kv_heads, max_seq, max_len, q_is_fp16;
+  int32_t tokens_per_block;          // set by the q.K^T launcher
+  int32_t tiles_per_block, n_parts;  // set by the softmax.V launcher
+  float sm_scale;
+  const void* q;
+  const uint16_t* k;  // fp16 [B][Hkv][S][D], keys after the rotary embedding
+  const uint16_t* v;  // fp16 [B][Hkv][S][D]
+  const int32_t* seq_len;
+  float* logits;   // [B][Hq][S]
+  float* partial;  // [B][Hq][n_parts][D + 2], as PvArgs
+  float* out;      // [B][Hq][D]
+};
+
 // Compute units of the current device (queried once per device, then cached).
 int device_cu_count();
 
@@ -78,5 +92,9 @@ hipError_t launch_append(int k_bits, int v_bits, const AppendArgs& a, hipStream_
 hipError_t launch_qk(int k_bits, int group, int batch, const QkArgs& a, hipStream_t s);
 hipError_t launch_qk_lut(int k_bits, int batch, const QkArgs& a, hipStream_t s);
 hipError_t launch_pv(int v_bits, int group, int batch, const PvArgs& a, hipStream_t s);
+// Log-sum-exp merge of the (o, m, l) partials in a.partial into a.out (used by launch_pv).
+hipError_t launch_pv_combine(int batch, const PvArgs& a, hipStream_t s);
+hipError_t launch_fp16_qk(int group, int batch, const Fp16Args& a, hipStream_t s);
+hipError_t launch_fp16_pv(int group, int batch, const Fp16Args& a, hipStream_t s);
 
 }  // namespace kvq

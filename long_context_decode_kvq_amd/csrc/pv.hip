@@ -372,11 +372,15 @@ hipError_t launch_pv_t(int batch, const PvArgs& a0, hipStream_t s) {
   hipLaunchKernelGGL((pv_partial_kernel<VB, G>), grid, dim3(kThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(pv_combine_kernel, dim3(a.n_q_heads, batch), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_pv_combine(batch, a, s);
 }
 
 }  // namespace
+
+hipError_t launch_pv_combine(int batch, const PvArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(pv_combine_kernel, dim3(a.n_q_heads, batch), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_pv(int v_bits, int group, int batch, const PvArgs& a, hipStream_t s) {
 #define KVQ_PV_CASE(VB, G) \

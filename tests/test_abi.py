@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(kvq.LIB_PATH), reason="libkvq
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
@@ -92,3 +92,20 @@ def test_entry_points_reject_before_launch():
     assert lib.kvq_qk_matvec(ctypes.byref(shape), ctypes.byref(fake), 4096, 0, 1.0, 4096, 257, None) == -1
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert lib.kvq_status_string(s)
+
+
+def test_fp16_baseline_entry_points_reject_before_launch():
+    lib = kvq.load_library()
+    c = cfg()
+    shape = c.shape()
+    p = 4096  # fake device pointers, never dereferenced: every case fails its host checks
+    assert lib.kvq_fp16_qk_matvec(ctypes.byref(shape), None, p, p, 0, 1.0, p, 10, None) == -1
+    assert lib.kvq_fp16_qk_matvec(ctypes.byref(shape), p, p, p, 2, 1.0, p, 10, None) == -1
+    assert lib.kvq_fp16_qk_matvec(ctypes.byref(shape), p, p, p, 0, 1.0, p, c.max_seq + 1, None) == -1
+    assert lib.kvq_fp16_pv_matvec(ctypes.byref(shape), p, p, p, p, p, 16, 10, None) == -4
+    assert lib.kvq_fp16_pv_matvec(ctypes.byref(shape), p, None, p, p, p, 1 << 20, 10, None) == -1
+    bad = cfg(head_dim=64).shape()
+    assert lib.kvq_fp16_qk_matvec(ctypes.byref(bad), p, p, p, 0, 1.0, p, 10, None) == -2
+    # bit widths and outliers do not concern the fp16 cache
+    odd = cfg(k_bits=5, n_outliers=-1).shape()
+    assert lib.kvq_fp16_pv_matvec(ctypes.byref(odd), p, p, p, p, p, 16, 10, None) == -4
