@@ -221,28 +221,45 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
         *cell = make_int2(0, 0);
       }
     }
-    // Dense part: lane = channel pair; the token weights come from lane t as scalars.
+    // Dense part: lane = channel pair.  The token weights enter as fp16 pairs (w_t, w_t+1),
+    // one scalar operand per two tokens of a packed dot product with the fp16 codebook pair
+    // (cb[a], cb[b]) (both products exact in fp32, fp32 accumulation).  Each tile's weights
+    // are scaled by 2^sh, which puts the tile's largest weight in [2^13, 2^14): every weight
+    // whose rounding matters is then a normal fp16 number, so its relative error is at most
+    // 2^-11 and the output's at most 2^-11 sum_t p_t |v~_t,c|; 2^-sh is undone exactly after
+    // the tile.
+    float unsc[G];
+    uint32_t wpair[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float wmax = wave_max_f32(wts[h]);
+      const int ex = wmax > 0.0f ? static_cast<int>((__builtin_bit_cast(uint32_t, wmax) >> 23) & 0xffu) - 127 : 0;
+      const int sh = min(max(13 - ex, -100), 100);  // 2^sh * wmax in [2^13, 2^14)
+      unsc[h] = __builtin_bit_cast(float, static_cast<uint32_t>(127 - sh) << 23);
+      const float ws = wts[h] * __builtin_bit_cast(float, static_cast<uint32_t>(127 + sh) << 23);
+      const uint32_t wh = __builtin_bit_cast(uint16_t, static_cast<_Float16>(ws));
+      const uint32_t wn = dpp_u32<0xF5>(wh);  // quad_perm [1,1,3,3]: lane 2m gets lane 2m + 1
+      wpair[h] = wh | (wn << 16);             // in lane 2m: (w_2m, w_2m+1)
+    }
+    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
     float accp[G][2][2];
 #pragma unroll
     for (int h = 0; h < G; ++h) accp[h][0][0] = accp[h][0][1] = accp[h][1][0] = accp[h][1][1] = 0.0f;
     static_for<0, kTile / 2>([&](auto mc) {
       constexpr int mm = decltype(mc)::value;
-      const uint32_t e0 = lut2[field<2 * VB, 2 * VB * mm>(d.w)];
-      const uint32_t e1 = lut2[field<2 * VB, kChanBits + 2 * VB * mm>(d.w)];
-      const float v0a = half_bits_to_float(e0 & 0xffffu), v0b = half_bits_to_float(e0 >> 16);
-      const float v1a = half_bits_to_float(e1 & 0xffffu), v1b = half_bits_to_float(e1 >> 16);
+      const half2_t e0 = __builtin_bit_cast(half2_t, lut2[field<2 * VB, 2 * VB * mm>(d.w)]);
+      const half2_t e1 = __builtin_bit_cast(half2_t, lut2[field<2 * VB, kChanBits + 2 * VB * mm>(d.w)]);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float wa = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wts[h]), 2 * mm));
-        const float wb = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wts[h]), 2 * mm + 1));
-        accp[h][0][mm & 1] = fmaf(v0b, wb, fmaf(v0a, wa, accp[h][0][mm & 1]));
-        accp[h][1][mm & 1] = fmaf(v1b, wb, fmaf(v1a, wa, accp[h][1][mm & 1]));
+        const half2_t wp = __builtin_bit_cast(half2_t, __builtin_amdgcn_readlane(static_cast<int>(wpair[h]), 2 * mm));
+        accp[h][0][mm & 1] = __builtin_amdgcn_fdot2(e0, wp, accp[h][0][mm & 1], false);
+        accp[h][1][mm & 1] = __builtin_amdgcn_fdot2(e1, wp, accp[h][1][mm & 1], false);
       }
     });
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      acc[h][0] += accp[h][0][0] + accp[h][0][1];
-      acc[h][1] += accp[h][1][0] + accp[h][1][1];
+      acc[h][0] = fmaf(accp[h][0][0] + accp[h][0][1], unsc[h], acc[h][0]);
+      acc[h][1] = fmaf(accp[h][1][0] + accp[h][1][1], unsc[h], acc[h][1]);
     }
     wave_lds_sync();  // the cleared cells are written before the next tile's atomics
   };
