@@ -338,6 +338,17 @@ def main():
         kern_events["qk"].append((e0, e1))
         kern_events["pv"].append((e1, e2))
     torch.cuda.synchronize()
+    # the single-pass kernel (one query head per kv head, 2/3-bit keys) on the same layers
+    fused_events = []
+    if wl.group == 1 and wl.k_bits <= 3:
+        for _ in range(args.kernel_steps):
+            e0, e1 = ev(), ev()
+            e0.record()
+            for lay in layers:
+                kvq.fused_decode_attention(lay["cache"], lay["q"], lay["bufs"].out, lay["bufs"].workspace, max_len=L_now)
+            e1.record()
+            fused_events.append((e0, e1))
+        torch.cuda.synchronize()
 
     # bytes: lengths grow by n_new per step; use the mean length over the timed steps
     L_mean = start_len + wl.n_new * (args.steps + 1) / 2.0
@@ -385,6 +396,10 @@ def main():
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
+    if fused_events:
+        fms = sum(a.elapsed_time(b) for a, b in fused_events) / (len(fused_events) * n_lay)
+        line["fused_single_pass"] = {"ms_per_layer": round(fms, 5), "two_call_ms_per_layer": round(kt["qk"] + kt["pv"], 5),
+                                     "gbs": round((qk_bk + pv_bk - 8 * wl.batch * wl.n_q_heads * L_now) / (fms * 1e-3) / 1e9, 1)}
     if args.fp16_baseline:
         line["fp16_baseline"] = fp16_baseline(wl, cfg, L_now, args.kernel_steps, kt)
     if args.traffic_probe:

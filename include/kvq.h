@@ -157,6 +157,19 @@ int kvq_pv_matvec(const kvq_shape* shape, const kvq_cache* cache, const float* l
                   void* workspace, size_t workspace_bytes, int32_t max_len, hipStream_t stream);
 
 /*
+ * Single-pass decode attention: kvq_qk_matvec followed by kvq_pv_matvec in one kernel
+ * pass (plus the combine), without writing the logits (summary page, abstract paragraph:
+ * decode is bandwidth-bound, and the logits are the one intermediate both passes move).
+ *   q, sm_scale, out, workspace, max_len  as for kvq_qk_matvec and kvq_pv_matvec; out
+ *   equals kvq_pv_matvec's output after kvq_qk_matvec (up to float rounding order).
+ * Supported: one query head per kv head (n_q_heads == n_kv_heads) and 2- or 3-bit keys;
+ * other shapes return KVQ_ERR_UNSUPPORTED and enqueue nothing (use the two calls).
+ */
+int kvq_decode_attention(const kvq_shape* shape, const kvq_cache* cache, const void* q, int32_t q_is_fp16,
+                         float sm_scale, float* out, void* workspace, size_t workspace_bytes, int32_t max_len,
+                         hipStream_t stream);
+
+/*
  * Uncompressed fp16 decode attention over a plain fp16 cache: the comparison point the
  * pages quote the compressed kernels against (summary page, abstract paragraph: custom
  * kernels faster than fp16 matrix-vector products).  Same logits and outputs as

@@ -22,7 +22,7 @@ KVQ_OK = 0
 STATUS_NAMES = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID", -2: "KVQ_ERR_UNSUPPORTED",
                 -3: "KVQ_ERR_CAPACITY", -4: "KVQ_ERR_WORKSPACE", -5: "KVQ_ERR_HIP"}
 EXPORTED = ("kvq_cache_sizes", "kvq_workspace_bytes", "kvq_quantize_append", "kvq_qk_matvec",
-            "kvq_pv_matvec", "kvq_fp16_qk_matvec", "kvq_fp16_pv_matvec", "kvq_status_string",
+            "kvq_pv_matvec", "kvq_decode_attention", "kvq_fp16_qk_matvec", "kvq_fp16_pv_matvec", "kvq_status_string",
             "kvq_abi_version")
 ABI_VERSION = 1
 
@@ -78,6 +78,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_pv_matvec.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(CacheDesc), P, P, P, SZ,
                                   I32, P]
     lib.kvq_pv_matvec.restype = ctypes.c_int
+    lib.kvq_decode_attention.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(CacheDesc), P, I32, ctypes.c_float,
+                                         P, P, SZ, I32, P]
+    lib.kvq_decode_attention.restype = ctypes.c_int
     lib.kvq_fp16_qk_matvec.argtypes = [ctypes.POINTER(Shape), P, P, P, I32, ctypes.c_float, P, I32, P]
     lib.kvq_fp16_qk_matvec.restype = ctypes.c_int
     lib.kvq_fp16_pv_matvec.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, SZ, I32, P]
@@ -247,6 +250,25 @@ def pv_matvec(cache: KVCache, logits: torch.Tensor, out: torch.Tensor, workspace
                                       logits.data_ptr(), out.data_ptr(), workspace.data_ptr(),
                                       workspace.numel() * workspace.element_size(), ml, _stream(stream))
     _check("kvq_pv_matvec", st)
+
+
+def fused_decode_attention(cache: KVCache, q: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                           sm_scale: float | None = None, max_len: int | None = None, stream=None) -> torch.Tensor:
+    """kvq_decode_attention: q [B][Hq][D] fp32/fp16 -> out fp32 [B][Hq][D] in one pass
+    (one query head per kv head, 2/3-bit keys)."""
+    cfg = cache.cfg
+    assert q.shape == (cfg.batch, cfg.n_q_heads, cfg.head_dim) and q.is_contiguous()
+    assert q.dtype in (torch.float32, torch.float16)
+    assert out.dtype == torch.float32 and out.numel() == cfg.batch * cfg.n_q_heads * cfg.head_dim
+    assert out.is_contiguous() and workspace.is_contiguous()
+    sm = 1.0 / math.sqrt(cfg.head_dim) if sm_scale is None else float(sm_scale)
+    ml = max(max(cache.lengths), 1) if max_len is None else int(max_len)
+    st = load_library().kvq_decode_attention(ctypes.byref(cache._shape), ctypes.byref(cache._desc), q.data_ptr(),
+                                             1 if q.dtype == torch.float16 else 0, sm, out.data_ptr(),
+                                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                             ml, _stream(stream))
+    _check("kvq_decode_attention", st)
+    return out
 
 
 class DecodeBuffers:

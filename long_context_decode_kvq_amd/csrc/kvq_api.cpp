@@ -42,6 +42,58 @@ int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
 
 size_t n_chunks_for(int32_t max_len) { return (static_cast<size_t>(max_len) + kvq::kPvChunk - 1) / kvq::kPvChunk; }
 
+kvq::QkArgs make_qk_args(const kvq_shape* s, const kvq_cache* c, const void* q, int32_t q_is_fp16, float sm_scale,
+                         float* logits, int32_t max_len) {
+  kvq::QkArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.n_q_heads = s->n_q_heads;
+  a.n_kv_heads = s->n_kv_heads;
+  a.max_seq = s->max_seq;
+  a.n_outliers = s->n_outliers;
+  a.max_len = max_len;
+  a.q_is_fp16 = q_is_fp16;
+  a.sm_scale = sm_scale;
+  // theta_i = base^(-2i/D); stored in revolutions so that the kernels reduce phases exactly
+  const double theta_log2 = std::log2(static_cast<double>(s->rope_base)) * 2.0 / s->head_dim;
+  for (int i = 0; i < kvq::kHalf; ++i) {
+    a.theta_rev[i] = std::exp2(-i * theta_log2) / (2.0 * M_PI);
+    int e = 0;
+    const double m = std::frexp(a.theta_rev[i], &e);  // theta_rev = m 2^e, m in [0.5, 1)
+    a.th_hi[i] = static_cast<float>(std::ldexp(std::nearbyint(std::ldexp(m, 15)), e - 15));
+    a.th_lo[i] = static_cast<float>(a.theta_rev[i] - static_cast<double>(a.th_hi[i]));
+  }
+  a.q = q;
+  a.k_codes = c->k_codes;
+  a.k_idx = c->k_out_idx;
+  a.k_val = c->k_out_val;
+  a.k_scale = c->k_scale;
+  a.k_cb = c->k_codebook;
+  a.seq_len = c->seq_len;
+  a.logits = logits;
+  return a;
+}
+
+kvq::PvArgs make_pv_args(const kvq_shape* s, const kvq_cache* c, const float* logits, float* out, void* workspace,
+                         int32_t max_len) {
+  kvq::PvArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.n_q_heads = s->n_q_heads;
+  a.n_kv_heads = s->n_kv_heads;
+  a.max_seq = s->max_seq;
+  a.n_outliers = s->n_outliers;
+  a.max_len = max_len;
+  a.logits = logits;
+  a.v_codes = c->v_codes;
+  a.v_idx = c->v_out_idx;
+  a.v_val = c->v_out_val;
+  a.v_scale = c->v_scale;
+  a.v_cb = c->v_codebook;
+  a.seq_len = c->seq_len;
+  a.partial = static_cast<float*>(workspace);
+  a.out = out;
+  return a;
+}
+
 }  // namespace
 
 namespace kvq {
@@ -172,32 +224,7 @@ int kvq_qk_matvec(const kvq_shape* s, const kvq_cache* c, const void* q, int32_t
   if (!c->k_codes || !c->k_scale || !c->k_codebook || !q || !logits) return KVQ_ERR_INVALID;
   if (q_is_fp16 != 0 && q_is_fp16 != 1) return KVQ_ERR_INVALID;
   if (max_len < 1 || max_len > s->max_seq || !std::isfinite(sm_scale)) return KVQ_ERR_INVALID;
-  kvq::QkArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.n_q_heads = s->n_q_heads;
-  a.n_kv_heads = s->n_kv_heads;
-  a.max_seq = s->max_seq;
-  a.n_outliers = s->n_outliers;
-  a.max_len = max_len;
-  a.q_is_fp16 = q_is_fp16;
-  a.sm_scale = sm_scale;
-  // theta_i = base^(-2i/D); stored in revolutions so that the kernels reduce phases exactly
-  const double theta_log2 = std::log2(static_cast<double>(s->rope_base)) * 2.0 / s->head_dim;
-  for (int i = 0; i < kvq::kHalf; ++i) {
-    a.theta_rev[i] = std::exp2(-i * theta_log2) / (2.0 * M_PI);
-    int e = 0;
-    const double m = std::frexp(a.theta_rev[i], &e);  // theta_rev = m 2^e, m in [0.5, 1)
-    a.th_hi[i] = static_cast<float>(std::ldexp(std::nearbyint(std::ldexp(m, 15)), e - 15));
-    a.th_lo[i] = static_cast<float>(a.theta_rev[i] - static_cast<double>(a.th_hi[i]));
-  }
-  a.q = q;
-  a.k_codes = c->k_codes;
-  a.k_idx = c->k_out_idx;
-  a.k_val = c->k_out_val;
-  a.k_scale = c->k_scale;
-  a.k_cb = c->k_codebook;
-  a.seq_len = c->seq_len;
-  a.logits = logits;
+  const kvq::QkArgs a = make_qk_args(s, c, q, q_is_fp16, sm_scale, logits, max_len);
   // One query head per kv head: the table-driven kernel for 2- and 3-bit keys (for 4-bit
   // keys the DPP kernel is faster: 120 against 134 us on the 128K layer).
   if (s->n_q_heads == s->n_kv_heads && s->k_bits <= 3) return hip_status(kvq::launch_qk_lut(s->k_bits, s->batch, a, stream));
@@ -213,23 +240,25 @@ int kvq_pv_matvec(const kvq_shape* s, const kvq_cache* c, const float* logits, f
   if (!c->v_codes || !c->v_scale || !c->v_codebook || !logits || !out) return KVQ_ERR_INVALID;
   if (max_len < 1 || max_len > s->max_seq) return KVQ_ERR_INVALID;
   if (!workspace || workspace_bytes < kvq_workspace_bytes(s, max_len)) return KVQ_ERR_WORKSPACE;
-  kvq::PvArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.n_q_heads = s->n_q_heads;
-  a.n_kv_heads = s->n_kv_heads;
-  a.max_seq = s->max_seq;
-  a.n_outliers = s->n_outliers;
-  a.max_len = max_len;
-  a.logits = logits;
-  a.v_codes = c->v_codes;
-  a.v_idx = c->v_out_idx;
-  a.v_val = c->v_out_val;
-  a.v_scale = c->v_scale;
-  a.v_cb = c->v_codebook;
-  a.seq_len = c->seq_len;
-  a.partial = static_cast<float*>(workspace);
-  a.out = out;
+  const kvq::PvArgs a = make_pv_args(s, c, logits, out, workspace, max_len);
   return hip_status(kvq::launch_pv(s->v_bits, s->n_q_heads / s->n_kv_heads, s->batch, a, stream));
+}
+
+int kvq_decode_attention(const kvq_shape* s, const kvq_cache* c, const void* q, int32_t q_is_fp16, float sm_scale,
+                         float* out, void* workspace, size_t workspace_bytes, int32_t max_len, hipStream_t stream) {
+  int st = check_shape(s);
+  if (st != KVQ_OK) return st;
+  st = check_cache_common(s, c);
+  if (st != KVQ_OK) return st;
+  if (!c->k_codes || !c->k_scale || !c->k_codebook || !c->v_codes || !c->v_scale || !c->v_codebook || !q || !out)
+    return KVQ_ERR_INVALID;
+  if (q_is_fp16 != 0 && q_is_fp16 != 1) return KVQ_ERR_INVALID;
+  if (max_len < 1 || max_len > s->max_seq || !std::isfinite(sm_scale)) return KVQ_ERR_INVALID;
+  if (s->n_q_heads != s->n_kv_heads || s->k_bits > 3) return KVQ_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < kvq_workspace_bytes(s, max_len)) return KVQ_ERR_WORKSPACE;
+  const kvq::QkArgs a = make_qk_args(s, c, q, q_is_fp16, sm_scale, nullptr, max_len);
+  const kvq::PvArgs p = make_pv_args(s, c, nullptr, out, workspace, max_len);
+  return hip_status(kvq::launch_fused(s->k_bits, s->v_bits, s->batch, a, p, stream));
 }
 
 // ---- uncompressed fp16 baseline --------------------------------------------------------

@@ -94,6 +94,9 @@ hipError_t launch_qk_lut(int k_bits, int batch, const QkArgs& a, hipStream_t s);
 hipError_t launch_pv(int v_bits, int group, int batch, const PvArgs& a, hipStream_t s);
 // Log-sum-exp merge of the (o, m, l) partials in a.partial into a.out (used by launch_pv).
 hipError_t launch_pv_combine(int batch, const PvArgs& a, hipStream_t s);
+// Single-pass q.K^T + softmax.V for one query head per kv head, 2/3-bit keys: QkArgs
+// supplies the key side (logits unused), PvArgs the value side and the workspace.
+hipError_t launch_fused(int k_bits, int v_bits, int batch, const QkArgs& a, const PvArgs& p, hipStream_t s);
 hipError_t launch_fp16_qk(int group, int batch, const Fp16Args& a, hipStream_t s);
 hipError_t launch_fp16_pv(int group, int batch, const Fp16Args& a, hipStream_t s);
 

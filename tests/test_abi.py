@@ -109,3 +109,18 @@ def test_fp16_baseline_entry_points_reject_before_launch():
     # bit widths and outliers do not concern the fp16 cache
     odd = cfg(k_bits=5, n_outliers=-1).shape()
     assert lib.kvq_fp16_pv_matvec(ctypes.byref(odd), p, p, p, p, p, 16, 10, None) == -4
+
+
+def test_fused_entry_point_rejects_before_launch():
+    lib = kvq.load_library()
+    p = 4096  # fake device pointers, never dereferenced
+    fake = kvq.CacheDesc(*([ctypes.c_void_p(p)] * len(kvq.CacheDesc._fields_)))
+    mha = cfg(n_q_heads=2, n_kv_heads=2, k_bits=3).shape()
+    assert lib.kvq_decode_attention(ctypes.byref(mha), None, p, 0, 1.0, p, p, 1 << 20, 10, None) == -1
+    assert lib.kvq_decode_attention(ctypes.byref(mha), ctypes.byref(fake), p, 0, 1.0, p, p, 16, 10, None) == -4
+    assert lib.kvq_decode_attention(ctypes.byref(mha), ctypes.byref(fake), p, 2, 1.0, p, p, 1 << 20, 10, None) == -1
+    # grouped heads and 4-bit keys are served by the two-call path
+    gqa = cfg(k_bits=3).shape()
+    assert lib.kvq_decode_attention(ctypes.byref(gqa), ctypes.byref(fake), p, 0, 1.0, p, p, 1 << 20, 10, None) == -2
+    k4 = cfg(n_q_heads=2, n_kv_heads=2, k_bits=4).shape()
+    assert lib.kvq_decode_attention(ctypes.byref(k4), ctypes.byref(fake), p, 0, 1.0, p, p, 1 << 20, 10, None) == -2

@@ -99,6 +99,31 @@ def test_qk_and_pv_parity(built):
     print(f"{name}: worst logit rel err {worst_l:.2e}, worst output rel err {worst_o:.2e}")
 
 
+def test_fused_decode_matches_oracle(built):
+    """The single-pass kernel (no logits written) against the oracle, within the output
+    criterion, for every case it serves (one query head per kv head, 2/3-bit keys); other
+    shapes are refused before launch."""
+    import long_context_decode_kvq_amd as kvq
+    name, case, cache = built
+    out = torch.full((case.wl.batch, case.wl.n_q_heads, D), float("nan"), device="cuda")
+    ws = torch.empty(kvq.workspace_bytes(cache.cfg, cache.cfg.max_seq) // 4, dtype=torch.float32, device="cuda")
+    if case.wl.group != 1 or case.wl.k_bits > 3:
+        with pytest.raises(kvq.KvqError):
+            kvq.fused_decode_attention(cache, case.q, out, ws)
+        return
+    kvq.fused_decode_attention(cache, case.q, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    worst = 0.0
+    for b in range(case.wl.batch):
+        for hq in range(case.wl.n_q_heads):
+            h = hq // case.wl.group
+            ref_l, ref_o = case.oracle_decode(b, hq)
+            scale_o = oracle.output_tolerance_scale(ref_l, case.oracle_stream(b, h), case.cbv)
+            worst = max(worst, assert_out_close(got[b, hq], ref_o, scale_o, what=f"fused {name} b={b} hq={hq}"))
+    print(f"fused {name}: worst output rel err {worst:.2e}")
+
+
 def test_decode_is_deterministic(built):
     """Logits are bitwise reproducible.  The value pass adds outlier corrections into LDS
     with atomics, so its fp32 summation order may vary between runs: two runs may differ
