@@ -46,7 +46,15 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   constexpr int kChanBits = 64 * VB;
   constexpr int kPairEntries = 1 << (2 * VB);
 
+  // With 2-bit values one byte (four consecutive tokens of a channel) indexes a 256-entry
+  // table of the four fp16 codebook values; otherwise a field of two tokens indexes a table
+  // of fp16 pairs.  (A 4096-entry quad table for 3-bit values measured slower: its 32 KB
+  // cost resident blocks and its random reads conflict.)
+  constexpr bool kQuad = VB == 2;
+  constexpr int kQuadEntries = kQuad ? 1 << (4 * VB) : 1;
   __shared__ uint32_t lut2[kPairEntries];         // fp16 (cb[a], cb[b]) for a token pair
+  __shared__ uint2 lut4[kQuadEntries];            // fp16 (cb[a], cb[b], cb[c], cb[d]) for a token quad
+  __shared__ uint32_t cbs[kNc];                   // fp16 codebook (for building lut4)
   __shared__ float osp[kWaves][G][kHeadDim];      // per-wave outlier corrections past the first two
   __shared__ int osi[kWaves][G][kHeadDim];        // per-wave, per-tile fixed-point outlier sums
   __shared__ float wm[kWaves][G], wl[kWaves][G];  // per-wave max and sum
@@ -131,12 +139,21 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   load(w_lo, bufA);  // unconditional, so the compiler counts the loads in flight exactly
 
   lut2[tid & (kPairEntries - 1)] = cb_a | (cb_b << 16);  // threads sharing an entry write the same value
+  if (kQuad && tid < kNc) cbs[tid] = cb_a;               // cb_a = cb[tid] for tid < 2^VB
   for (int e = tid; e < kWaves * G * kHeadDim; e += kThreads) {
     (&osp[0][0][0])[e] = 0.0f;
     (&osi[0][0][0])[e] = 0;
   }
   const float zc = zero_code_value<kNc>(cb_lo, lane);  // value every outlier slot decodes to
   block_lds_barrier();
+  if constexpr (kQuad) {
+    constexpr uint32_t m = kNc - 1;
+    for (int e = tid; e < kQuadEntries; e += kThreads) {
+      const uint32_t c0 = cbs[e & m], c1 = cbs[(e >> VB) & m], c2 = cbs[(e >> (2 * VB)) & m], c3 = cbs[(e >> (3 * VB)) & m];
+      lut4[e] = make_uint2(c0 | (c1 << 16), c2 | (c3 << 16));
+    }
+    block_lds_barrier();
+  }
 
 
   float m_run[G], lsum[G], acc[G][2];
@@ -245,17 +262,34 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
     float accp[G][2][2];
 #pragma unroll
     for (int h = 0; h < G; ++h) accp[h][0][0] = accp[h][0][1] = accp[h][1][0] = accp[h][1][1] = 0.0f;
-    static_for<0, kTile / 2>([&](auto mc) {
-      constexpr int mm = decltype(mc)::value;
-      const half2_t e0 = __builtin_bit_cast(half2_t, lut2[field<2 * VB, 2 * VB * mm>(d.w)]);
-      const half2_t e1 = __builtin_bit_cast(half2_t, lut2[field<2 * VB, kChanBits + 2 * VB * mm>(d.w)]);
+    if constexpr (kQuad) {
+      static_for<0, kTile / 4>([&](auto qc) {
+        constexpr int qq = decltype(qc)::value;
+        const uint2 e0 = lut4[field<4 * VB, 4 * VB * qq>(d.w)];
+        const uint2 e1 = lut4[field<4 * VB, kChanBits + 4 * VB * qq>(d.w)];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const half2_t wp = __builtin_bit_cast(half2_t, __builtin_amdgcn_readlane(static_cast<int>(wpair[h]), 2 * mm));
-        accp[h][0][mm & 1] = __builtin_amdgcn_fdot2(e0, wp, accp[h][0][mm & 1], false);
-        accp[h][1][mm & 1] = __builtin_amdgcn_fdot2(e1, wp, accp[h][1][mm & 1], false);
-      }
-    });
+        for (int h = 0; h < G; ++h) {
+          const half2_t wlo = __builtin_bit_cast(half2_t, __builtin_amdgcn_readlane(static_cast<int>(wpair[h]), 4 * qq));
+          const half2_t whi = __builtin_bit_cast(half2_t, __builtin_amdgcn_readlane(static_cast<int>(wpair[h]), 4 * qq + 2));
+          accp[h][0][0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e0.x), wlo, accp[h][0][0], false);
+          accp[h][0][1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e0.y), whi, accp[h][0][1], false);
+          accp[h][1][0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e1.x), wlo, accp[h][1][0], false);
+          accp[h][1][1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e1.y), whi, accp[h][1][1], false);
+        }
+      });
+    } else {
+      static_for<0, kTile / 2>([&](auto mc) {
+        constexpr int mm = decltype(mc)::value;
+        const half2_t e0 = __builtin_bit_cast(half2_t, lut2[field<2 * VB, 2 * VB * mm>(d.w)]);
+        const half2_t e1 = __builtin_bit_cast(half2_t, lut2[field<2 * VB, kChanBits + 2 * VB * mm>(d.w)]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const half2_t wp = __builtin_bit_cast(half2_t, __builtin_amdgcn_readlane(static_cast<int>(wpair[h]), 2 * mm));
+          accp[h][0][mm & 1] = __builtin_amdgcn_fdot2(e0, wp, accp[h][0][mm & 1], false);
+          accp[h][1][mm & 1] = __builtin_amdgcn_fdot2(e1, wp, accp[h][1][mm & 1], false);
+        }
+      });
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       acc[h][0] = fmaf(accp[h][0][0] + accp[h][0][1], unsc[h], acc[h][0]);
