@@ -35,6 +35,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp16-baseline", dest="fp16_baseline", action="store_false",
                    help="skip timing the uncompressed fp16 kernels at the same shape")
+    p.add_argument("--no-fused", dest="fused", action="store_false",
+                   help="skip timing the single-pass kernel (profiling runs of the two-call path)")
     p.add_argument("--cpu-heads", type=int, default=32, help="kv-head streams per layer the oracle times in the CPU leg")
     p.add_argument("--cpu-layers", type=int, default=4, help="layers the oracle times in the CPU leg")
     p.add_argument("--kernel-steps", type=int, default=5,
@@ -98,10 +100,10 @@ def counter_means(d, counter):
         for row in csv.DictReader(open(f)):
             if row.get("Counter_Name") != counter:
                 continue
-            m = re.search(r"(qk_lut_kernel|qk_kernel|pv_partial_kernel|pv_combine_kernel|append_kernel|bitwise_not)",
+            m = re.search(r"::(qk_lut_kernel|qk_kernel|pv_partial_kernel|pv_combine_kernel|append_kernel)\b|(bitwise_not)",
                           row.get("Kernel_Name", ""))
             if m:
-                acc.setdefault(m.group(1), []).append(float(row["Counter_Value"]))
+                acc.setdefault(m.group(1) or m.group(2), []).append(float(row["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
@@ -340,7 +342,7 @@ def main():
     torch.cuda.synchronize()
     # the single-pass kernel (one query head per kv head, 2/3-bit keys) on the same layers
     fused_events = []
-    if wl.group == 1 and wl.k_bits <= 3:
+    if args.fused and wl.group == 1 and wl.k_bits <= 3:
         for _ in range(args.kernel_steps):
             e0, e1 = ev(), ev()
             e0.record()
