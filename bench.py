@@ -73,15 +73,15 @@ def source_hash(names):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel, src_hash):
-    """HBM bytes per launch measured with rocprofv3 counters, if the committed
-    measurement was taken on the current kernel source; else None."""
+def traffic_from_profile(workload, kernel, src_hash):
+    """HBM bytes per launch measured with rocprofv3 counters on this workload, if the
+    committed measurement was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    e = t.get(kernel)
+    e = t.get(workload, {}).get(kernel)
     if not e or e.get("source_hash") != src_hash:
         return None
     return e.get("hbm_bytes_per_launch")
@@ -107,7 +107,7 @@ def counter_means(d, counter):
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
-def summarize_counters(fetch_dir, write_dir):
+def summarize_counters(fetch_dir, write_dir, workload):
     """HBM bytes per launch = FETCH_SIZE and WRITE_SIZE (KiB per dispatch) each scaled by the
     factor that maps the same counter of the calibration kernel onto its known bytes."""
     fetch, write = counter_means(fetch_dir, "FETCH_SIZE"), counter_means(write_dir, "WRITE_SIZE")
@@ -126,8 +126,15 @@ def summarize_counters(fetch_dir, write_dir):
         out[name] = {"source_hash": source_hash(src), "fetch_kib": fk, "write_kib": wk,
                      "hbm_bytes_per_launch": round(fk * 1024.0 * f_scale + wk * 1024.0 * w_scale)}
     path = os.path.join(ROOT, "profiles", "traffic.json")
+    allw = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            allw = json.load(f)
+        if "calibration" in allw:  # single-workload layout of older files
+            allw = {}
+    allw[workload] = out
     with open(path, "w") as f:
-        json.dump(out, f, indent=1)
+        json.dump(allw, f, indent=1)
     print(json.dumps(out, indent=1))
 
 
@@ -228,7 +235,7 @@ def fp16_baseline(wl, cfg, L, kernel_steps, kt, n_layers=4):
 def main():
     args = parse()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        summarize_counters(*args.summarize_counters, args.workload)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
@@ -368,7 +375,7 @@ def main():
     qk_name, qk_src = (("qk_lut_kernel", "qk_lut.hip") if wl.group == 1 and wl.k_bits <= 3 else ("qk_kernel", "qk.hip"))
     dom_name = {"qk": qk_name, "pv": "pv_partial_kernel+pv_combine_kernel"}[dom]
     src = {"qk": [qk_src, "kvq_device.h"], "pv": ["pv.hip", "kvq_device.h"]}[dom]
-    traffic = traffic_from_profile(dom_name, source_hash(src))
+    traffic = traffic_from_profile(args.workload, dom_name, source_hash(src))
 
     line = {
         "metric": "quantized-KV decode attention: achieved HBM GB/s (% of peak) + KV-tokens/s",
