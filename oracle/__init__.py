@@ -2,7 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
 benchmark's CPU-baseline leg, never by the product path.  It shares no code with the
-HIP library.  Parity status of each function is listed in ``oracle/kvquant.py``.
+HIP library.  Parity status of each function is listed in ``oracle/kvquant.py`` and
+``oracle/codebook_fit.py``.
 """
 from .kvquant import *  # noqa: F401,F403
 from .kvquant import (StreamCache, attend, decode_head, dequant_keys, dequant_values,
@@ -11,3 +12,4 @@ from .kvquant import (StreamCache, attend, decode_head, dequant_keys, dequant_va
                       quantize_keys, quantize_stream, quantize_values, rope, rope_frequencies,
                       select_outliers, softmax, unpack_key_records, unpack_value_tiles,
                       zero_code)
+from .codebook_fit import clamp_inputs, finalize, fit_codebook, fit_init, fit_step, fixed_point, quantization_mse

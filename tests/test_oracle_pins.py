@@ -347,3 +347,65 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     with pytest.raises(AssertionError):
         test_nearest_code_matches_exact_rational_argmin(3)
     monkeypatch.setattr(oracle, "nearest_code", good_nc)
+
+
+# ---- codebook fitting (unweighted k-means, oracle/codebook_fit.py) -----------------------
+
+def test_fit_uniform_inputs_keep_the_uniform_quantizer():
+    """For inputs spread evenly over [-1, 1] the optimal K-level quantizer (Lloyd-Max) has
+    its levels at the midpoints of K equal bins: iterating must not move them."""
+    from fractions import Fraction
+    n = 1 << 14
+    u = np.array([(i + 0.5) / n * 2.0 - 1.0 for i in range(n)], dtype=np.float32)
+    for bits in (2, 3, 4):
+        k = 1 << bits
+        c = oracle.fit_init(bits)
+        for _ in range(5):
+            c = oracle.fit_step(u, c)[0]
+        expect = [float(Fraction(-1) + Fraction(2 * j + 1, k)) for j in range(k)]
+        assert np.allclose(c.astype(np.float64), expect, atol=1e-6), (bits, c)
+
+
+def test_fit_moves_each_centroid_to_its_cluster_mean():
+    """Tight clusters, one inside each initial bin: one iteration puts every centroid on
+    its cluster's exact mean (rational arithmetic), to the float32 rounding."""
+    from fractions import Fraction
+    rng = np.random.default_rng(7)
+    for bits in (2, 3, 4):
+        k = 1 << bits
+        width = 2.0 / k
+        centers = -1.0 + width * (np.arange(k) + 0.5 + rng.uniform(-0.3, 0.3, k))
+        pts = [np.float32(c + rng.uniform(-0.02, 0.02, rng.integers(5, 40)) * width).astype(np.float32) for c in centers]
+        u = np.concatenate(pts)
+        c1 = oracle.fit_step(u, oracle.fit_init(bits))[0]
+        for j, p in enumerate(pts):
+            mean = float(sum(Fraction(float(x)) for x in p) / len(p))
+            assert abs(float(c1[j]) - mean) <= 2e-7 * max(1.0, abs(mean)), (bits, j)
+
+
+def test_fit_distortion_never_increases():
+    """Lloyd's invariant: neither the assignment nor the mean update can raise the mean
+    squared error."""
+    rng = np.random.default_rng(3)
+    u = oracle.clamp_inputs(rng.standard_normal(20000) * 0.4)
+    for bits in (2, 3, 4):
+        c = oracle.fit_init(bits)
+        prev = oracle.quantization_mse(u, c)
+        for _ in range(8):
+            c = oracle.fit_step(u, c)[0]
+            cur = oracle.quantization_mse(u, c)
+            assert cur <= prev + 1e-12, (bits, cur, prev)
+            prev = cur
+
+
+def test_fit_empty_cluster_keeps_its_centroid_and_result_is_a_valid_codebook():
+    u = np.full(100, 0.3, dtype=np.float32)  # every input in one bin
+    c1, sums, counts, _ = oracle.fit_step(u, oracle.fit_init(2))
+    assert counts.tolist() == [0, 0, 100, 0]
+    assert c1[0] == oracle.fit_init(2)[0] and c1[3] == oracle.fit_init(2)[3]
+    assert abs(float(c1[2]) - 0.3) < 1e-7
+    for cand in ([0.5, 0.5, 0.5, 1.0], [0.999, 1.0, 1.0, 1.0], [-1.0, -1.0, 0.2, 0.2]):
+        h = oracle.finalize(np.array(cand, dtype=np.float32))
+        assert np.all(np.diff(h.astype(np.float64)) > 0) and h.min() >= -1 and h.max() <= 1, (cand, h)
+        # values already in place are kept
+        assert h[0] == np.float16(cand[0]) or cand[0] > 0.99
