@@ -35,6 +35,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp16-baseline", dest="fp16_baseline", action="store_false",
                    help="skip timing the uncompressed fp16 kernels at the same shape")
+    p.add_argument("--no-codebook-fit", dest="codebook_fit", action="store_false",
+                   help="skip timing the codebook fit on the layer's key calibration set")
     p.add_argument("--no-fused", dest="fused", action="store_false",
                    help="skip timing the single-pass kernel (profiling runs of the two-call path)")
     p.add_argument("--cpu-heads", type=int, default=32, help="kv-head streams per layer the oracle times in the CPU leg")
@@ -186,6 +188,33 @@ def cpu_layer(wl, seed, n_heads, L, sm):
                                wl.rope_base, sm)
         elapsed += time.perf_counter() - t0
     return elapsed
+
+
+def codebook_fit_leg(wl, seed, iters=20, n_calib=4096):
+    """Codebook fit (k-means) on the key calibration set of one layer: every kv head's
+    n_calib calibration tokens divided by the per-channel key scale, fitted for wl.k_bits."""
+    import torch
+
+    import long_context_decode_kvq_amd as kvq
+    import synth
+    ks = torch.from_numpy(synth.key_scale(seed, wl)).cuda()
+    u = torch.cat([(synth.keys(seed, wl, 0, h, n_calib, "cuda").float() / ks[h]).reshape(-1)
+                   for h in range(wl.n_kv_heads)]).contiguous()
+    out = torch.empty(1 << wl.k_bits, dtype=torch.float16, device="cuda")
+    ws = torch.empty(int(kvq.load_library().kvq_fit_workspace_bytes()), dtype=torch.uint8, device="cuda")
+    kvq.fit_codebook(u, wl.k_bits, iters, out, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        kvq.fit_codebook(u, wl.k_bits, iters, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 3
+    per_iter = ms / iters
+    return {"inputs": u.numel(), "bits": wl.k_bits, "iterations": iters, "ms": round(ms, 4),
+            "ms_per_iteration": round(per_iter, 5), "gbs_per_pass": round(4 * u.numel() / (per_iter * 1e-3) / 1e9, 1),
+            "codebook": [float(x) for x in out.float().cpu()]}
 
 
 def fp16_baseline(wl, cfg, L, kernel_steps, kt, n_layers=4):
@@ -409,6 +438,8 @@ def main():
         fms = sum(a.elapsed_time(b) for a, b in fused_events) / (len(fused_events) * n_lay)
         line["fused_single_pass"] = {"ms_per_layer": round(fms, 5), "two_call_ms_per_layer": round(kt["qk"] + kt["pv"], 5),
                                      "gbs": round((qk_bk + pv_bk - 8 * wl.batch * wl.n_q_heads * L_now) / (fms * 1e-3) / 1e9, 1)}
+    if args.codebook_fit:
+        line["codebook_fit"] = codebook_fit_leg(wl, args.seed * 1000)
     if args.fp16_baseline:
         line["fp16_baseline"] = fp16_baseline(wl, cfg, L_now, args.kernel_steps, kt)
     if args.traffic_probe:

@@ -170,6 +170,30 @@ int kvq_decode_attention(const kvq_shape* shape, const kvq_cache* cache, const v
                          hipStream_t stream);
 
 /*
+ * Per-layer codebook fitting (summary page, abstract paragraph, technique (iii); paper
+ * note, item (3)): unweighted 1-D k-means over normalised calibration activations (keys
+ * divided by their per-channel scale, values by their per-vector scale), the input of a
+ * layer's k_codebook or v_codebook.  The pages weight the fit by each activation's
+ * sensitivity, which needs a trained model; this is the unweighted version.
+ *   u             device float32 [n] (n < 2^33; NULL allowed for n = 0), clamped to [-1, 1].
+ *   bits          2, 3 or 4: 2^bits entries.
+ *   iters         Lloyd iterations (>= 0), starting from the midpoints -1 + (2j+1)/2^bits.
+ *                 Each iteration assigns every input to its nearest entry by the quantizer's
+ *                 own rule (smallest j minimising the float32 |u - c_j|) and moves each entry
+ *                 with inputs to their mean, formed exactly from the inputs rounded to the
+ *                 grid 2^-30 (so the result does not depend on the order of summation):
+ *                 c_j = float32(sum / (count * 2^30)); an entry without inputs stays.
+ *   codebook_out  device fp16 bits [2^bits]: the entries rounded to fp16, then raised where
+ *                 needed to at least the next fp16 above their predecessor and, if the last
+ *                 passes 1, lowered from the top: strictly ascending, within [-1, 1].
+ *   workspace     device scratch of at least kvq_fit_workspace_bytes() bytes.
+ * Errors as elsewhere; KVQ_ERR_UNSUPPORTED for bits outside {2, 3, 4}.
+ */
+size_t kvq_fit_workspace_bytes(void);
+int kvq_fit_codebook(const float* u, int64_t n, int32_t bits, int32_t iters, uint16_t* codebook_out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Uncompressed fp16 decode attention over a plain fp16 cache: the comparison point the
  * pages quote the compressed kernels against (summary page, abstract paragraph: custom
  * kernels faster than fp16 matrix-vector products).  Same logits and outputs as

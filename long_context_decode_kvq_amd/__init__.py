@@ -22,7 +22,8 @@ KVQ_OK = 0
 STATUS_NAMES = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID", -2: "KVQ_ERR_UNSUPPORTED",
                 -3: "KVQ_ERR_CAPACITY", -4: "KVQ_ERR_WORKSPACE", -5: "KVQ_ERR_HIP"}
 EXPORTED = ("kvq_cache_sizes", "kvq_workspace_bytes", "kvq_quantize_append", "kvq_qk_matvec",
-            "kvq_pv_matvec", "kvq_decode_attention", "kvq_fp16_qk_matvec", "kvq_fp16_pv_matvec", "kvq_status_string",
+            "kvq_pv_matvec", "kvq_decode_attention", "kvq_fit_workspace_bytes", "kvq_fit_codebook",
+            "kvq_fp16_qk_matvec", "kvq_fp16_pv_matvec", "kvq_status_string",
             "kvq_abi_version")
 ABI_VERSION = 1
 
@@ -81,6 +82,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_decode_attention.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(CacheDesc), P, I32, ctypes.c_float,
                                          P, P, SZ, I32, P]
     lib.kvq_decode_attention.restype = ctypes.c_int
+    lib.kvq_fit_workspace_bytes.argtypes = []
+    lib.kvq_fit_workspace_bytes.restype = SZ
+    lib.kvq_fit_codebook.argtypes = [P, ctypes.c_int64, I32, I32, P, P, SZ, P]
+    lib.kvq_fit_codebook.restype = ctypes.c_int
     lib.kvq_fp16_qk_matvec.argtypes = [ctypes.POINTER(Shape), P, P, P, I32, ctypes.c_float, P, I32, P]
     lib.kvq_fp16_qk_matvec.restype = ctypes.c_int
     lib.kvq_fp16_pv_matvec.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, SZ, I32, P]
@@ -347,3 +352,19 @@ def fp16_decode_attention(cache: Fp16Cache, q: torch.Tensor, bufs: DecodeBuffers
     fp16_qk_matvec(cache, q, bufs.logits, sm_scale, max_len, stream)
     fp16_pv_matvec(cache, bufs.logits, bufs.out, bufs.workspace, max_len, stream)
     return bufs.out
+
+
+def fit_codebook(u: torch.Tensor, bits: int, iters: int, out: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_fit_codebook: float32 device activations (already divided by their scale) ->
+    fp16 codebook of 2^bits entries (a float16 tensor)."""
+    assert u.dtype == torch.float32 and u.is_contiguous()
+    lib = load_library()
+    if out is None:
+        out = torch.empty(1 << bits, dtype=torch.float16, device=u.device)
+    if workspace is None:
+        workspace = torch.empty(int(lib.kvq_fit_workspace_bytes()), dtype=torch.uint8, device=u.device)
+    st = lib.kvq_fit_codebook(u.data_ptr() if u.numel() else None, u.numel(), int(bits), int(iters), out.data_ptr(),
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("kvq_fit_codebook", st)
+    return out

@@ -261,6 +261,19 @@ int kvq_decode_attention(const kvq_shape* s, const kvq_cache* c, const void* q, 
   return hip_status(kvq::launch_fused(s->k_bits, s->v_bits, s->batch, a, p, stream));
 }
 
+// ---- codebook fitting ---------------------------------------------------------------
+
+size_t kvq_fit_workspace_bytes(void) { return kvq::fit_workspace_bytes(); }
+
+int kvq_fit_codebook(const float* u, int64_t n, int32_t bits, int32_t iters, uint16_t* codebook_out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  if (!bits_ok(bits)) return KVQ_ERR_UNSUPPORTED;
+  if (n < 0 || n >= (static_cast<int64_t>(1) << 33) || iters < 0 || !codebook_out) return KVQ_ERR_INVALID;
+  if (n > 0 && !u) return KVQ_ERR_INVALID;
+  if (!workspace || workspace_bytes < kvq::fit_workspace_bytes()) return KVQ_ERR_WORKSPACE;
+  return hip_status(kvq::launch_fit_codebook(bits, u, n, iters, codebook_out, workspace, stream));
+}
+
 // ---- uncompressed fp16 baseline --------------------------------------------------------
 
 static int check_fp16_shape(const kvq_shape* s) {

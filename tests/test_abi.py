@@ -124,3 +124,16 @@ def test_fused_entry_point_rejects_before_launch():
     assert lib.kvq_decode_attention(ctypes.byref(gqa), ctypes.byref(fake), p, 0, 1.0, p, p, 1 << 20, 10, None) == -2
     k4 = cfg(n_q_heads=2, n_kv_heads=2, k_bits=4).shape()
     assert lib.kvq_decode_attention(ctypes.byref(k4), ctypes.byref(fake), p, 0, 1.0, p, p, 1 << 20, 10, None) == -2
+
+
+def test_fit_codebook_entry_point_rejects_before_launch():
+    lib = kvq.load_library()
+    p, ws = 4096, int(lib.kvq_fit_workspace_bytes())
+    assert ws >= 320
+    assert lib.kvq_fit_codebook(p, 10, 5, 3, p, p, ws, None) == -2        # bits
+    assert lib.kvq_fit_codebook(None, 10, 3, 3, p, p, ws, None) == -1     # inputs missing
+    assert lib.kvq_fit_codebook(p, -1, 3, 3, p, p, ws, None) == -1        # negative count
+    assert lib.kvq_fit_codebook(p, 10, 3, -1, p, p, ws, None) == -1       # negative iterations
+    assert lib.kvq_fit_codebook(p, 1 << 33, 3, 1, p, p, ws, None) == -1   # integer sums could overflow
+    assert lib.kvq_fit_codebook(p, 10, 3, 3, None, p, ws, None) == -1     # no output
+    assert lib.kvq_fit_codebook(p, 10, 3, 3, p, p, ws - 1, None) == -4    # workspace
