@@ -323,3 +323,23 @@ def output_tolerance_scale(logits, cache: StreamCache, v_codebook32, length: int
     vd = dequant_values(cache.v_codes[:n], cache.v_idx[:n], cache.v_val[:n], cache.v_scale[:n],
                         v_codebook32)
     return softmax(logits[:n]) @ np.abs(vd)
+
+
+# ----------------------------------------------------------------------------------
+# Key scale calibration
+# ----------------------------------------------------------------------------------
+
+
+def key_scale_from_keys(k16, k: int = 0) -> np.ndarray:
+    """Per-channel key scale from calibration keys [P1 (i): keys are quantized per channel;
+    P2 item (1)]: s_c = max over the given vectors of |x_c| (float32, exact for fp16
+    inputs).  With k > 0 each vector's k outliers (``select_outliers``) are left out first,
+    so the scale covers the dense part the quantizer sees (the reading in which outliers
+    are held aside before the range is set).  k16: [N, D] fp16 vectors of one kv head."""
+    x = _as_f16(k16)
+    mag = np.abs(x.astype(np.float32))
+    if k > 0:
+        idx = select_outliers(x, k)
+        mag = mag.copy()
+        np.put_along_axis(mag, idx, 0.0, axis=1)
+    return mag.max(axis=0) if len(mag) else np.zeros(x.shape[1], dtype=np.float32)

@@ -409,3 +409,22 @@ def test_fit_empty_cluster_keeps_its_centroid_and_result_is_a_valid_codebook():
         assert np.all(np.diff(h.astype(np.float64)) > 0) and h.min() >= -1 and h.max() <= 1, (cand, h)
         # values already in place are kept
         assert h[0] == np.float16(cand[0]) or cand[0] > 0.99
+
+
+def test_key_scale_is_the_channel_max_of_the_dense_part():
+    """Brute force on small inputs: for every channel, the largest |x| among the entries
+    that are not one of their vector's k largest (ties to the lower channel)."""
+    rng = np.random.default_rng(5)
+    for k in (0, 1, 2, 5):
+        x = rng.standard_normal((40, 16)).astype(np.float16)
+        x[3, :] = np.float16(2.0)  # a vector of ties: its outliers are its lowest channels
+        got = oracle.key_scale_from_keys(x, k)
+        exp = np.zeros(16)
+        for t in range(40):
+            row = [(abs(float(x[t, c])), c) for c in range(16)]
+            out = {c for _, c in sorted(row, key=lambda e: (-e[0], e[1]))[:k]}
+            for c in range(16):
+                if c not in out:
+                    exp[c] = max(exp[c], abs(float(x[t, c])))
+        assert np.array_equal(got.astype(np.float64), exp), k
+    assert np.array_equal(oracle.key_scale_from_keys(x, 16), np.zeros(16, np.float32))
