@@ -190,6 +190,35 @@ def cpu_layer(wl, seed, n_heads, L, sm):
     return elapsed
 
 
+def key_scale_leg(wl, cfg, seed):
+    """Per-channel key scale over a whole prompt of the workload (the keys a prefill
+    appends), each vector's outliers left out; returns the time and the bytes read per
+    second."""
+    import torch
+
+    import long_context_decode_kvq_amd as kvq
+    import synth
+    n = wl.seq_len
+    keys = torch.empty(wl.batch, n, wl.n_kv_heads, wl.head_dim, dtype=torch.float16, device="cuda")
+    for b in range(wl.batch):
+        for h in range(wl.n_kv_heads):
+            keys[b, :, h] = synth.keys(seed, wl, b, h, n, "cuda")
+    out = torch.empty(wl.n_kv_heads, wl.head_dim, dtype=torch.float32, device="cuda")
+    kvq.key_scale(cfg, keys, True, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        kvq.key_scale(cfg, keys, True, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    nbytes = keys.numel() * 2
+    del keys
+    return {"tokens": wl.batch * n, "exclude_outliers": True, "ms": round(ms, 4),
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def codebook_fit_leg(wl, seed, iters=20, n_calib=4096):
     """Codebook fit (k-means) on the key calibration set of one layer: every kv head's
     n_calib calibration tokens divided by the per-channel key scale, fitted for wl.k_bits."""
@@ -439,6 +468,7 @@ def main():
         line["fused_single_pass"] = {"ms_per_layer": round(fms, 5), "two_call_ms_per_layer": round(kt["qk"] + kt["pv"], 5),
                                      "gbs": round((qk_bk + pv_bk - 8 * wl.batch * wl.n_q_heads * L_now) / (fms * 1e-3) / 1e9, 1)}
     if args.codebook_fit:
+        line["key_scale_calibration"] = key_scale_leg(wl, cfg, args.seed * 1000 + 7)
         line["codebook_fit"] = codebook_fit_leg(wl, args.seed * 1000)
     if args.fp16_baseline:
         line["fp16_baseline"] = fp16_baseline(wl, cfg, L_now, args.kernel_steps, kt)

@@ -170,6 +170,21 @@ int kvq_decode_attention(const kvq_shape* shape, const kvq_cache* cache, const v
                          hipStream_t stream);
 
 /*
+ * Per-channel key scale from a bulk of calibration keys (summary page, abstract paragraph,
+ * technique (i); paper note, item (1)): k_scale[h][c] = max |x_c| over every vector of kv
+ * head h in `keys`, e.g. a prompt before its prefill append.
+ *   keys              fp16 [B][n_tokens][Hkv][D], before the rotary embedding (the layout
+ *                     kvq_quantize_append takes).
+ *   exclude_outliers  0: over all entries; 1: over each vector's dense part, its
+ *                     shape->n_outliers largest-magnitude entries (ties to the lower
+ *                     channel, as the quantizer selects them) left out.
+ *   k_scale_out       device float32 [Hkv][D]; overwritten (zeros for n_tokens = 0).
+ * The max is exact: the result is bit-for-bit the maximum fp16 magnitude.
+ */
+int kvq_key_scale(const kvq_shape* shape, const uint16_t* keys, int32_t n_tokens, int32_t exclude_outliers,
+                  float* k_scale_out, hipStream_t stream);
+
+/*
  * Per-layer codebook fitting (summary page, abstract paragraph, technique (iii); paper
  * note, item (3)): unweighted 1-D k-means over normalised calibration activations (keys
  * divided by their per-channel scale, values by their per-vector scale), the input of a

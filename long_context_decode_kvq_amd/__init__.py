@@ -22,7 +22,7 @@ KVQ_OK = 0
 STATUS_NAMES = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID", -2: "KVQ_ERR_UNSUPPORTED",
                 -3: "KVQ_ERR_CAPACITY", -4: "KVQ_ERR_WORKSPACE", -5: "KVQ_ERR_HIP"}
 EXPORTED = ("kvq_cache_sizes", "kvq_workspace_bytes", "kvq_quantize_append", "kvq_qk_matvec",
-            "kvq_pv_matvec", "kvq_decode_attention", "kvq_fit_workspace_bytes", "kvq_fit_codebook",
+            "kvq_pv_matvec", "kvq_decode_attention", "kvq_key_scale", "kvq_fit_workspace_bytes", "kvq_fit_codebook",
             "kvq_fp16_qk_matvec", "kvq_fp16_pv_matvec", "kvq_status_string",
             "kvq_abi_version")
 ABI_VERSION = 1
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_decode_attention.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(CacheDesc), P, I32, ctypes.c_float,
                                          P, P, SZ, I32, P]
     lib.kvq_decode_attention.restype = ctypes.c_int
+    lib.kvq_key_scale.argtypes = [ctypes.POINTER(Shape), P, I32, I32, P, P]
+    lib.kvq_key_scale.restype = ctypes.c_int
     lib.kvq_fit_workspace_bytes.argtypes = []
     lib.kvq_fit_workspace_bytes.restype = SZ
     lib.kvq_fit_codebook.argtypes = [P, ctypes.c_int64, I32, I32, P, P, SZ, P]
@@ -367,4 +369,18 @@ def fit_codebook(u: torch.Tensor, bits: int, iters: int, out: torch.Tensor | Non
     st = lib.kvq_fit_codebook(u.data_ptr() if u.numel() else None, u.numel(), int(bits), int(iters), out.data_ptr(),
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
     _check("kvq_fit_codebook", st)
+    return out
+
+
+def key_scale(cfg: CacheConfig, keys: torch.Tensor, exclude_outliers: bool = False,
+              out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_key_scale: calibration keys fp16 [B][n][Hkv][D] -> float32 [Hkv][D] per-channel
+    scale (max |x|, over each vector's dense part with exclude_outliers)."""
+    assert keys.dtype == torch.float16 and keys.is_contiguous() and keys.dim() == 4
+    assert keys.shape[0] == cfg.batch and keys.shape[2] == cfg.n_kv_heads and keys.shape[3] == cfg.head_dim
+    if out is None:
+        out = torch.empty(cfg.n_kv_heads, cfg.head_dim, dtype=torch.float32, device=keys.device)
+    st = load_library().kvq_key_scale(ctypes.byref(cfg.shape()), keys.data_ptr() if keys.numel() else None,
+                                      keys.shape[1], 1 if exclude_outliers else 0, out.data_ptr(), _stream(stream))
+    _check("kvq_key_scale", st)
     return out

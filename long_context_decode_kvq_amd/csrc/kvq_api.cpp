@@ -261,6 +261,18 @@ int kvq_decode_attention(const kvq_shape* s, const kvq_cache* c, const void* q, 
   return hip_status(kvq::launch_fused(s->k_bits, s->v_bits, s->batch, a, p, stream));
 }
 
+// ---- calibration ----------------------------------------------------------------------
+
+int kvq_key_scale(const kvq_shape* s, const uint16_t* keys, int32_t n_tokens, int32_t exclude_outliers,
+                  float* k_scale_out, hipStream_t stream) {
+  int st = check_shape(s);
+  if (st != KVQ_OK) return st;
+  if (n_tokens < 0 || !k_scale_out || (n_tokens > 0 && !keys)) return KVQ_ERR_INVALID;
+  if (exclude_outliers != 0 && exclude_outliers != 1) return KVQ_ERR_INVALID;
+  return hip_status(kvq::launch_key_scale(keys, s->batch, n_tokens, s->n_kv_heads,
+                                          exclude_outliers ? s->n_outliers : 0, k_scale_out, stream));
+}
+
 // ---- codebook fitting ---------------------------------------------------------------
 
 size_t kvq_fit_workspace_bytes(void) { return kvq::fit_workspace_bytes(); }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace kvq {
 
 constexpr int kHeadDim = 128;
@@ -169,6 +171,29 @@ __device__ __forceinline__ float zero_code_value(uint32_t cb_bits, int lane) {
   const uint32_t key = lane < NC ? ((cb_bits & 0x7fffu) << 8) | static_cast<uint32_t>(lane) : 0xffffffffu;
   const uint32_t m = ~wave_max_u32(~key);  // wave minimum
   return half_bits_to_float(static_cast<uint32_t>(__shfl(static_cast<int>(cb_bits), static_cast<int>(m & 0xffu))) & 0xffffu);
+}
+
+// Selection key: fp16 magnitude bits above the inverted channel index, so the unsigned
+// maximum is the largest |x| and, among equal magnitudes, the lowest channel.
+__device__ __forceinline__ uint32_t outlier_key(uint32_t xbits, uint32_t c) {
+  return ((xbits & 0x7fffu) << 16) | (0xffffu - c);
+}
+
+// Marks the k largest-magnitude channels of the wave's vector (k <= 128).
+__device__ __forceinline__ void select_outliers(uint32_t key0, uint32_t key1, int k, bool& sel0,
+                                                bool& sel1) {
+  sel0 = false;
+  sel1 = false;
+  for (int r = 0; r < k; ++r) {
+    uint32_t m0 = sel0 ? 0u : key0;
+    uint32_t m1 = sel1 ? 0u : key1;
+    uint32_t m = wave_max_u32(m0 > m1 ? m0 : m1);
+    if (!sel0 && key0 == m) {
+      sel0 = true;
+    } else if (!sel1 && key1 == m) {
+      sel1 = true;
+    }
+  }
 }
 
 // LDS byte address of a pointer into shared memory.

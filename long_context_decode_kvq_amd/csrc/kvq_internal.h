@@ -98,6 +98,9 @@ hipError_t launch_pv_combine(int batch, const PvArgs& a, hipStream_t s);
 // supplies the key side (logits unused), PvArgs the value side and the workspace.
 hipError_t launch_fused(int k_bits, int v_bits, int batch, const QkArgs& a, const PvArgs& p, hipStream_t s);
 hipError_t launch_fp16_qk(int group, int batch, const Fp16Args& a, hipStream_t s);
+// Per-channel key scale (max |x| over calibration keys, optionally their dense parts).
+hipError_t launch_key_scale(const uint16_t* keys, int batch, int n_tokens, int n_kv_heads, int k, float* out,
+                            hipStream_t s);
 // Codebook fitting (k-means over normalised activations): workspace size and launcher.
 size_t fit_workspace_bytes();
 hipError_t launch_fit_codebook(int bits, const float* u, long long n, int iters, uint16_t* out, void* workspace,

@@ -137,3 +137,14 @@ def test_fit_codebook_entry_point_rejects_before_launch():
     assert lib.kvq_fit_codebook(p, 1 << 33, 3, 1, p, p, ws, None) == -1   # integer sums could overflow
     assert lib.kvq_fit_codebook(p, 10, 3, 3, None, p, ws, None) == -1     # no output
     assert lib.kvq_fit_codebook(p, 10, 3, 3, p, p, ws - 1, None) == -4    # workspace
+
+
+def test_key_scale_entry_point_rejects_before_launch():
+    lib = kvq.load_library()
+    shape = cfg().shape()
+    p = 4096
+    assert lib.kvq_key_scale(ctypes.byref(shape), None, 10, 0, p, None) == -1
+    assert lib.kvq_key_scale(ctypes.byref(shape), p, -1, 0, p, None) == -1
+    assert lib.kvq_key_scale(ctypes.byref(shape), p, 10, 2, p, None) == -1
+    assert lib.kvq_key_scale(ctypes.byref(shape), p, 10, 0, None, None) == -1
+    assert lib.kvq_key_scale(ctypes.byref(cfg(head_dim=64).shape()), p, 10, 0, p, None) == -2
