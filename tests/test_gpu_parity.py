@@ -222,3 +222,52 @@ def test_graph_replay_of_decode_step_matches_eager():
         o_g, o_e = bufs_g.out.cpu().numpy(), bufs_e.out.cpu().numpy()
         assert np.allclose(o_g, o_e, rtol=1e-5, atol=1e-6)
     assert torch.equal(cache_g.k_codes, cache_e.k_codes) and torch.equal(cache_g.v_codes, cache_e.v_codes)
+
+
+# name -> (workload, lens): several split parts per stream for every group size, plus an
+# empty sequence.
+MERGE_CASES = {
+    "g1": (_wl("llama7b_32k", batch=2, n_q_heads=2, n_kv_heads=2, seq_len=3000), [3000, 0]),
+    "g2": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=4, n_kv_heads=2, seq_len=2600), [2600, 0]),
+    "g4": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=4, n_kv_heads=1, seq_len=9000), [9000, 0]),
+    "g8": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=8, n_kv_heads=1, seq_len=5000), [5000, 0]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MERGE_CASES))
+def test_pv_split_merge_across_calls_on_one_workspace(name):
+    """softmax.V splits each stream over several blocks and merges their partials.  Two
+    logit sets from the oracle (A and -A) alternate on one workspace, with two grid sizes
+    (max_len = max_seq and = the longest length), so a partial left by the previous call
+    would show: every output must match the oracle's attention over the same float32
+    logits, and the empty sequence must give zeros."""
+    import long_context_decode_kvq_amd as kvq
+    wl, lens = MERGE_CASES[name]
+    case = Case(wl, seed=7, lens=lens, device="cuda")
+    cache = case.build_gpu()
+    n = int(lens[0])
+    S = cache.cfg.max_seq
+    la = np.zeros((wl.batch, wl.n_q_heads, S), np.float32)
+    for hq in range(wl.n_q_heads):
+        la[0, hq, :n] = case.oracle_decode(0, hq)[0].astype(np.float32)
+    expected = {}
+    for sign in (1.0, -1.0):
+        lg = (sign * la).astype(np.float32)
+        for hq in range(wl.n_q_heads):
+            c = case.oracle_stream(0, hq // wl.group)
+            vd = oracle.dequant_values(c.v_codes, c.v_idx, c.v_val, c.v_scale, case.cbv)
+            l64 = lg[0, hq, :n].astype(np.float64)
+            expected[sign, hq] = (oracle.attend(l64, vd), oracle.output_tolerance_scale(l64, c, case.cbv))
+    bufs = kvq.DecodeBuffers(cache)
+    dev = {s: torch.from_numpy(s * la).cuda() for s in (1.0, -1.0)}
+    for it in range(6):
+        for sign in (1.0, -1.0):
+            bufs.logits.copy_(dev[sign])
+            bufs.out.fill_(float("nan"))
+            kvq.pv_matvec(cache, bufs.logits, bufs.out, bufs.workspace, max_len=S if it % 2 == 0 else n)
+            torch.cuda.synchronize()
+            got = bufs.out.cpu().numpy()
+            for hq in range(wl.n_q_heads):
+                ref, scale = expected[sign, hq]
+                assert_out_close(got[0, hq], ref, scale, what=f"{name} it={it} sign={sign} hq={hq}")
+            assert np.all(got[1] == 0.0), f"{name}: empty sequence output not zero"
