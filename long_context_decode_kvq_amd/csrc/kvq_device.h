@@ -201,6 +201,29 @@ __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));
 }
 
+// Raw buffer access for streaming loads: a descriptor over the wave-uniform range
+// [base, base + bytes) (bytes < 2^32; base and size in scalar registers) read at a per-lane
+// 32-bit byte offset.  A kernel that rebuilds the descriptor for every tile at the tile's
+// first byte keeps its per-lane offsets fixed, so a load costs no vector arithmetic; a read
+// past the range returns zero instead of faulting.  0x00020000 is the gfx9-family third
+// descriptor word (raw, untyped dwords).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load_b32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load_u8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
 // cos/sin of 2*pi*r for a revolution count r already reduced to [0, 1).
 __device__ __forceinline__ void sincos_rev(float r, float* s, float* c) { sincospif(2.0f * r, s, c); }
 

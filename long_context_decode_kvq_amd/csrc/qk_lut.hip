@@ -45,7 +45,9 @@ struct LutRec {
   uint32_t oi[2], ov[2];  // its first two outliers: channels and fp16 value bits
 };
 
-template <int KB>
+// kExtra: outliers beyond the first kLutPrefetchOutliers per token exist (read in a loop
+// of their own); without them that loop is compiled out.
+template <int KB, bool kExtra>
 __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   using Sh = LutShape<KB>;
   constexpr int kNc = Sh::kNc;
@@ -88,27 +90,33 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   const int o_second = kp > 1 ? 1 : 0;
 
   // Every call issues the same loads at valid addresses (super-tile clamped to the block's
-  // range, tile to the buffer), so the compiler counts the loads in flight exactly.
+  // range, tile to the buffer), so the compiler counts the loads in flight exactly.  The
+  // loads go through buffer descriptors rebuilt per tile at the tile's first token (scalar
+  // arithmetic), with fixed per-lane offsets, so they cost no vector instructions.
+  const uint32_t rec_off = static_cast<uint32_t>(lane) * (16 * KB);
+  const uint32_t out_off = static_cast<uint32_t>(lane * o_stride);  // outlier entries before this lane's
+  const uint32_t second_off = out_off + o_second;
+  const uint32_t tile_outs = static_cast<uint32_t>(kTile * o_stride);  // outlier entries of a tile
   auto load_rec = [&](int s, LutRec<KB>& d) {
     s = min(s, s_hi - 1);
-    const int tile = min(kLutWaves * s + wave, tile_cap);
-    const size_t tok = static_cast<size_t>(tile) * kTile + lane;
-    const uint4* p = reinterpret_cast<const uint4*>(recs + tok * (16 * KB));
+    const int tile = min(kLutWaves * s + wave, tile_cap);  // wave-uniform
+    const size_t tok0 = static_cast<size_t>(tile) * kTile;
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(recs + tok0 * (16 * KB), kTile * 16 * KB);
 #pragma unroll
     for (int v = 0; v < KB; ++v) {
-      const uint4 q = p[v];
+      const u32x4 q = buf_load_b128(rr, rec_off + 16 * v);
       d.w[4 * v + 0] = q.x;
       d.w[4 * v + 1] = q.y;
       d.w[4 * v + 2] = q.z;
       d.w[4 * v + 3] = q.w;
     }
-    const size_t slot = stream * S + tok;
-    const uint8_t* i0 = o_idx + slot * o_stride;
-    const uint16_t* v0 = o_val + slot * o_stride;
-    d.oi[0] = i0[0];
-    d.oi[1] = i0[o_second];
-    d.ov[0] = v0[0];
-    d.ov[1] = v0[o_second];
+    const size_t slot0 = (stream * S + tok0) * o_stride;
+    const __amdgpu_buffer_rsrc_t ri = make_rsrc(o_idx + slot0, tile_outs + 1);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(o_val + slot0, 2 * tile_outs + 2);
+    d.oi[0] = buf_load_u8(ri, out_off);
+    d.oi[1] = buf_load_u8(ri, second_off);
+    d.ov[0] = buf_load_u16(rv, 2 * out_off);
+    d.ov[1] = buf_load_u16(rv, 2 * second_off);
   };
 
   // ---- set-up inputs, then the first two records ---------------------------------------
@@ -255,11 +263,14 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
     };
     if (kp >= 1) add_outlier(d.oi[0], d.ov[0]);
     if (kp >= 2) add_outlier(d.oi[1], d.ov[1]);
-    const int t = (kLutWaves * s + wave) * kTile + lane;
+    const int t0 = (kLutWaves * s + wave) * kTile;  // wave-uniform
+    const int t = t0 + lane;
     if (t < L) {
-      const size_t o = (stream * S + t) * k;
-      for (int j = kLutPrefetchOutliers; j < k; ++j) add_outlier(a.k_idx[o + j], a.k_val[o + j]);
-      a.logits[(static_cast<size_t>(seq) * a.n_q_heads + kvh) * S + t] = a.sm_scale * l;
+      if constexpr (kExtra) {
+        const size_t o = (stream * S + t) * k;
+        for (int j = kLutPrefetchOutliers; j < k; ++j) add_outlier(a.k_idx[o + j], a.k_val[o + j]);
+      }
+      (a.logits + (static_cast<size_t>(seq) * a.n_q_heads + kvh) * S + t0)[lane] = a.sm_scale * l;
     }
   };
 
@@ -282,12 +293,12 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   }
 }
 
-template <int KB>
+template <int KB, bool kExtra>
 hipError_t launch_qk_lut_t(int batch, const QkArgs& a0, hipStream_t st) {
   using Sh = LutShape<KB>;
   QkArgs a = a0;
   const size_t lds = Sh::kBufs * Sh::kBufBytes + kHeadDim * 4 + Sh::kBufs * kHalf * 8 + kHalf * 8;
-  static const bool attr_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&qk_lut_kernel<KB>),
+  static const bool attr_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&qk_lut_kernel<KB, kExtra>),
                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
                                                   static_cast<int>(lds)) == hipSuccess;
   if (!attr_ok) return hipErrorInvalidValue;
@@ -298,7 +309,7 @@ hipError_t launch_qk_lut_t(int batch, const QkArgs& a0, hipStream_t st) {
   const long streams = static_cast<long>(batch) * a.n_kv_heads;
   static const int resident = [&] {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&qk_lut_kernel<KB>),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&qk_lut_kernel<KB, kExtra>),
                                                      kLutThreads, lds) != hipSuccess || n < 1)
       n = 1;
     return n;
@@ -307,15 +318,16 @@ hipError_t launch_qk_lut_t(int batch, const QkArgs& a0, hipStream_t st) {
   const long per_stream = std::max(1L, std::min<long>((slots + streams - 1) / streams, supers));
   a.tiles_per_wave = static_cast<int>((supers + per_stream - 1) / per_stream);  // super-tiles per block
   dim3 grid((supers + a.tiles_per_wave - 1) / a.tiles_per_wave, a.n_kv_heads, batch);
-  hipLaunchKernelGGL((qk_lut_kernel<KB>), grid, dim3(kLutThreads), lds, st, a);
+  hipLaunchKernelGGL((qk_lut_kernel<KB, kExtra>), grid, dim3(kLutThreads), lds, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_qk_lut(int k_bits, int batch, const QkArgs& a, hipStream_t s) {
-  if (k_bits == 2) return launch_qk_lut_t<2>(batch, a, s);
-  if (k_bits == 3) return launch_qk_lut_t<3>(batch, a, s);
+  const bool extra = a.n_outliers > kLutPrefetchOutliers;
+  if (k_bits == 2) return extra ? launch_qk_lut_t<2, true>(batch, a, s) : launch_qk_lut_t<2, false>(batch, a, s);
+  if (k_bits == 3) return extra ? launch_qk_lut_t<3, true>(batch, a, s) : launch_qk_lut_t<3, false>(batch, a, s);
   return hipErrorInvalidValue;
 }
 
