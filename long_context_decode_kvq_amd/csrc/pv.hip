@@ -103,29 +103,37 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   const int o_second = kp > 1 ? 1 : 0;
 
   // Every call issues the same loads (a tile past the wave's run reloads its last tile,
-  // a cache hit), so the compiler can wait for exactly the tile being consumed.
+  // a cache hit), so the compiler can wait for exactly the tile being consumed.  The loads
+  // go through buffer descriptors rebuilt per tile at the tile's first token (scalar
+  // arithmetic) with fixed per-lane offsets, so they cost no vector instructions.
+  const uint32_t val_off = static_cast<uint32_t>(lane) * (16 * VB);
+  const uint32_t out_off = static_cast<uint32_t>(lane * o_stride);  // outlier entries before this lane's
+  const uint32_t second_off = out_off + o_second;
+  const uint32_t tile_outs = static_cast<uint32_t>(kTile * o_stride);
   auto load = [&](int tile, TileData<VB, G>& d) {
     tile = max(0, min(tile, w_hi - 1));  // a wave without tiles reads tile 0 (always valid)
-    const uint4* p = reinterpret_cast<const uint4*>(vtiles + static_cast<size_t>(tile) * (1024 * VB) + lane * (16 * VB));
+    const size_t t0 = static_cast<size_t>(tile) * kTile;  // wave-uniform; t0 + 64 <= max_seq
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(vtiles + static_cast<size_t>(tile) * (1024 * VB), 1024 * VB);
 #pragma unroll
     for (int v = 0; v < VB; ++v) {
-      const uint4 q = p[v];
+      const u32x4 q = buf_load_b128(rt, val_off + 16 * v);
       d.w[4 * v + 0] = q.x;
       d.w[4 * v + 1] = q.y;
       d.w[4 * v + 2] = q.z;
       d.w[4 * v + 3] = q.w;
     }
-    const int t = tile * kTile + lane;  // < max_seq, so every load below is in bounds
-    const size_t slot = stream * S + t;
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(lbase + t0, static_cast<uint32_t>(((G - 1) * static_cast<size_t>(S) + kTile) * 4));
 #pragma unroll
-    for (int h = 0; h < G; ++h) d.lg[h] = lbase[static_cast<size_t>(h) * S + t];
-    d.sv = a.v_scale[slot];
-    const uint8_t* i0 = o_idx + slot * o_stride;
-    const uint16_t* v0 = o_val + slot * o_stride;
-    d.oi[0] = i0[0];
-    d.oi[1] = i0[o_second];
-    d.ov[0] = v0[0];
-    d.ov[1] = v0[o_second];
+    for (int h = 0; h < G; ++h)
+      d.lg[h] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4u * lane, static_cast<uint32_t>(h * static_cast<size_t>(S) * 4), 0));
+    const size_t slot0 = stream * S + t0;
+    d.sv = buf_load_u16(make_rsrc(a.v_scale + slot0, 2 * kTile), 2u * lane);
+    const __amdgpu_buffer_rsrc_t ri = make_rsrc(o_idx + slot0 * o_stride, tile_outs + 1);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(o_val + slot0 * o_stride, 2 * tile_outs + 2);
+    d.oi[0] = buf_load_u8(ri, out_off);
+    d.oi[1] = buf_load_u8(ri, second_off);
+    d.ov[0] = buf_load_u16(rv, 2 * out_off);
+    d.ov[1] = buf_load_u16(rv, 2 * second_off);
   };
 
   // Set-up inputs first, then the wave's first tile, so that the tile's memory latency
