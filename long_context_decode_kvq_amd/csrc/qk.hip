@@ -114,24 +114,31 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   const size_t o_stride = kp > 0 ? k : 0;
   const int o_second = kp > 1 ? 1 : 0;
 
+  // Loads through buffer descriptors rebuilt per tile at the tile's first token (scalar
+  // arithmetic) with fixed per-lane offsets: no vector address arithmetic per tile.
+  const uint32_t rec_off = static_cast<uint32_t>(lane) * (16 * KB);
+  const uint32_t out_off = static_cast<uint32_t>(lane * o_stride);  // outlier entries before this lane's
+  const uint32_t second_off = out_off + o_second;
+  const uint32_t tile_outs = static_cast<uint32_t>(kTile * o_stride);
   auto load_rec = [&](int tile, Rec<KB>& d) {
     tile = min(tile, last_tile);  // past the run: reload the last tile (cache hit), keeps the load count fixed
-    const size_t slot = stream * S + static_cast<size_t>(tile) * kTile + lane;
-    const uint4* p = reinterpret_cast<const uint4*>(recs + (static_cast<size_t>(tile) * kTile + lane) * (16 * KB));
+    const size_t tok0 = static_cast<size_t>(tile) * kTile;  // wave-uniform
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(recs + tok0 * (16 * KB), kTile * 16 * KB);
 #pragma unroll
     for (int v = 0; v < KB; ++v) {
-      const uint4 q = p[v];
+      const u32x4 q = buf_load_b128(rr, rec_off + 16 * v);
       d.w[4 * v + 0] = q.x;
       d.w[4 * v + 1] = q.y;
       d.w[4 * v + 2] = q.z;
       d.w[4 * v + 3] = q.w;
     }
-    const uint8_t* i0 = o_idx + slot * o_stride;
-    const uint16_t* v0 = o_val + slot * o_stride;
-    d.oi[0] = i0[0];
-    d.oi[1] = i0[o_second];
-    d.ov[0] = v0[0];
-    d.ov[1] = v0[o_second];
+    const size_t slot0 = (stream * S + tok0) * o_stride;
+    const __amdgpu_buffer_rsrc_t ri = make_rsrc(o_idx + slot0, tile_outs + 1);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(o_val + slot0, 2 * tile_outs + 2);
+    d.oi[0] = buf_load_u8(ri, out_off);
+    d.oi[1] = buf_load_u8(ri, second_off);
+    d.ov[0] = buf_load_u16(rv, 2 * out_off);
+    d.ov[1] = buf_load_u16(rv, 2 * second_off);
   };
 
   // Query pairs this lane rotates every tile.  Slot j holds rotary pair
