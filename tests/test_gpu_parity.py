@@ -44,6 +44,12 @@ CASES = {
     "incremental_appends": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=4, n_kv_heads=2, seq_len=400),
                             [400, 257], [1, 62, 1, 64, 65, 3, 200, 1, 100]),
     "length_one": (_wl("single_head_4k", seq_len=1), [1], None),
+    # k = ceil(f D) = 5 and 3: the first two outliers of a token travel with its record, the
+    # rest go through the kernels' general loop
+    "mha2_3bit_k5": (_wl("llama7b_32k", n_q_heads=2, n_kv_heads=2, seq_len=1300, outlier_frac=0.035), [1300], None),
+    "mha2_2bit_k3": (_wl("llama7b_1m_2bit", n_q_heads=2, n_kv_heads=2, seq_len=1100, outlier_frac=0.02), [1100], None),
+    "gqa4_k5_ragged": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=4, n_kv_heads=1, seq_len=900, outlier_frac=0.035),
+                       [900, 333], None),
 }
 
 
