@@ -59,6 +59,11 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   __shared__ int osi[kWaves][G][kHeadDim];        // per-wave, per-tile fixed-point outlier sums
   __shared__ float wm[kWaves][G], wl[kWaves][G];  // per-wave max and sum
   __shared__ float wo[kWaves][G][kHeadDim];       // per-wave weighted sums
+  // With several query heads the tile's fp16 weight pairs are staged in LDS and read back
+  // at wave-uniform addresses (broadcast), four pairs per read, instead of one lane read
+  // (a VALU instruction) per pair and head; with one head the lane reads measured faster.
+  constexpr bool kStageW = G > 1;
+  __shared__ uint4 wst[kStageW ? kWaves : 1][G][kTile / 8];  // (w_2m, w_2m+1) at word m
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -265,7 +270,19 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
       const uint32_t wh = __builtin_bit_cast(uint16_t, static_cast<_Float16>(ws));
       const uint32_t wn = dpp_u32<0xF5>(wh);  // quad_perm [1,1,3,3]: lane 2m gets lane 2m + 1
       wpair[h] = wh | (wn << 16);             // in lane 2m: (w_2m, w_2m+1)
+      if (kStageW && (lane & 1) == 0) reinterpret_cast<uint32_t*>(&wst[kStageW ? wave : 0][h][0])[lane >> 1] = wpair[h];
     }
+    if constexpr (kStageW) wave_lds_sync();
+    // the weight pair of tokens (2m, 2m + 1) for head h, the same in every lane
+    auto wpair_of = [&](int h, auto mc) {
+      constexpr int m = decltype(mc)::value;
+      if constexpr (kStageW) {
+        const uint4 wq = wst[kStageW ? wave : 0][h][m / 4];
+        return (m & 3) == 0 ? wq.x : (m & 3) == 1 ? wq.y : (m & 3) == 2 ? wq.z : wq.w;
+      } else {
+        return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wpair[h]), 2 * m));
+      }
+    };
     typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
     float accp[G][2][2];
 #pragma unroll
@@ -277,8 +294,8 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
         const uint2 e1 = lut4[field<4 * VB, kChanBits + 4 * VB * qq>(d.w)];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const half2_t wlo = __builtin_bit_cast(half2_t, __builtin_amdgcn_readlane(static_cast<int>(wpair[h]), 4 * qq));
-          const half2_t whi = __builtin_bit_cast(half2_t, __builtin_amdgcn_readlane(static_cast<int>(wpair[h]), 4 * qq + 2));
+          const half2_t wlo = __builtin_bit_cast(half2_t, wpair_of(h, std::integral_constant<int, 2 * qq>{}));
+          const half2_t whi = __builtin_bit_cast(half2_t, wpair_of(h, std::integral_constant<int, 2 * qq + 1>{}));
           accp[h][0][0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e0.x), wlo, accp[h][0][0], false);
           accp[h][0][1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e0.y), whi, accp[h][0][1], false);
           accp[h][1][0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e1.x), wlo, accp[h][1][0], false);
@@ -292,7 +309,7 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
         const half2_t e1 = __builtin_bit_cast(half2_t, lut2[field<2 * VB, kChanBits + 2 * VB * mm>(d.w)]);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const half2_t wp = __builtin_bit_cast(half2_t, __builtin_amdgcn_readlane(static_cast<int>(wpair[h]), 2 * mm));
+          const half2_t wp = __builtin_bit_cast(half2_t, wpair_of(h, mc));
           accp[h][0][mm & 1] = __builtin_amdgcn_fdot2(e0, wp, accp[h][0][mm & 1], false);
           accp[h][1][mm & 1] = __builtin_amdgcn_fdot2(e1, wp, accp[h][1][mm & 1], false);
         }
