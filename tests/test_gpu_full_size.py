@@ -60,6 +60,11 @@ def test_full_layer_sampled_heads(name):
     bufs.logits.fill_(float("nan"))
     kvq.qk_matvec(cache, q, bufs.logits, max_len=S)
     kvq.pv_matvec(cache, bufs.logits, bufs.out, bufs.workspace, max_len=S)
+    fused = None
+    if wl.group == 1 and wl.k_bits <= 3:  # the single-pass kernel on the same cache
+        fused = torch.full_like(bufs.out, float("nan"))
+        ws = torch.empty(kvq.workspace_bytes(cfg, S) // 4, dtype=torch.float32, device="cuda")
+        kvq.fused_decode_attention(cache, q, fused, ws, max_len=S)
     torch.cuda.synchronize()
     assert cache.seq_len.cpu().tolist() == [n] * wl.batch
     sm = 1.0 / math.sqrt(D)
@@ -82,4 +87,8 @@ def test_full_layer_sampled_heads(name):
             assert torch.isnan(bufs.logits[b, hq, n:]).all(), "logits written past seq_len"
             scale_o = oracle.output_tolerance_scale(ref_l, c, cbv)
             wo_err = assert_out_close(bufs.out[b, hq].cpu().numpy(), ref_o, scale_o, what=f"{what} hq={hq}")
-            print(f"{what} hq={hq}: worst logit rel err {wl_err:.2e}, worst output rel err {wo_err:.2e}")
+            msg = f"{what} hq={hq}: worst logit rel err {wl_err:.2e}, worst output rel err {wo_err:.2e}"
+            if fused is not None:
+                wf_err = assert_out_close(fused[b, hq].cpu().numpy(), ref_o, scale_o, what=f"{what} hq={hq} single-pass")
+                msg += f", single-pass {wf_err:.2e}"
+            print(msg)
