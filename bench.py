@@ -140,10 +140,24 @@ def summarize_counters(fetch_dir, write_dir, workload):
     print(json.dumps(out, indent=1))
 
 
-def cpu_baseline(wl, seed, n_heads, n_layers):
+def cpu_model():
+    """The host CPU's model name (Linux), or the platform string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(wl, seed, n_streams, n_layers):
     """Time the oracle (as it stands) on a bounded sample of the same step: the decode-step
-    append and full-length decode attention for n_heads (sequence, kv head) streams of each
-    of n_layers layers; report the rate scaled to algorithmic bytes per second."""
+    append and full-length decode attention for n_streams (sequence, kv head) streams of
+    each of n_layers layers, on one thread; report the rate scaled to algorithmic bytes
+    per second."""
     import torch
     from threadpoolctl import threadpool_limits
 
@@ -153,41 +167,77 @@ def cpu_baseline(wl, seed, n_heads, n_layers):
     with threadpool_limits(limits=1):
         torch.set_num_threads(1)
         for li in range(n_layers):
-            elapsed += cpu_layer(wl, seed + li, n_heads, L, sm)
-    qk, pv, app = algorithmic_bytes(wl, L + 1)
-    per_stream = (qk + pv + app) / (wl.batch * wl.n_kv_heads)
-    return {"value": round(per_stream * n_heads * n_layers / elapsed / 1e9, 6), "unit": "GB/s", "cores": 1,
+            for i in range(n_streams):
+                elapsed += cpu_stream(wl, seed + li, i, L, sm)
+    return {"value": round(stream_bytes(wl) * n_streams * n_layers / elapsed / 1e9, 6), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{n_heads} of {wl.batch * wl.n_kv_heads} kv-head streams x {n_layers} layers, L={L + 1}: "
-                      f"append of the new token + float64 decode attention, {elapsed:.1f} s, 1 thread"}
+            "sample": f"{n_streams} of {wl.batch * wl.n_kv_heads} kv-head streams x {n_layers} layers, L={L + 1}: "
+                      f"append of the new token + float64 decode attention, {elapsed:.1f} s, 1 thread, "
+                      f"{cpu_model()}"}
 
 
-def cpu_layer(wl, seed, n_heads, L, sm):
-    """Oracle seconds for one layer's sample (the untimed prefix quantization excluded)."""
+def cpu_baseline_parallel(wl, seed, n_streams, n_layers, workers):
+    """The same sample spread over `workers` single-threaded processes (spawned, so they
+    share nothing with this process's GPU state).  Each worker times its streams as the
+    serial leg does; the slowest worker's timed total is the parallel run's time."""
+    import multiprocessing as mp
+
+    L = wl.seq_len
+    sm = 1.0 / math.sqrt(wl.head_dim)
+    tasks = [(wl, seed + li, i, L, sm) for li in range(n_layers) for i in range(n_streams)]
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(workers, initializer=_cpu_worker_init, initargs=(wl, seed, sm)) as pool:
+        timed = pool.starmap(_cpu_worker_task, [(w, tasks[w::workers]) for w in range(workers)])
+    slowest = max(timed)
+    return {"value": round(stream_bytes(wl) * len(tasks) / slowest / 1e9, 6), "unit": "GB/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"the serial leg's sample over {workers} single-threaded processes: slowest worker "
+                      f"{slowest:.2f} s of timed oracle work (total {sum(timed):.1f} s), {cpu_model()}"}
+
+
+def _cpu_worker_init(wl, seed, sm):
+    from threadpoolctl import threadpool_limits
+    import torch
+    threadpool_limits(limits=1)
+    torch.set_num_threads(1)
+    cpu_stream(wl, seed, 0, 64, sm)  # untimed warm-up of the oracle's code paths
+
+
+def _cpu_worker_task(w, tasks):
+    return sum(cpu_stream(*t) for t in tasks)
+
+
+def stream_bytes(wl):
+    """Algorithmic bytes of one (sequence, kv head) stream's share of a decode step."""
+    qk, pv, app = algorithmic_bytes(wl, wl.seq_len + 1)
+    return (qk + pv + app) / (wl.batch * wl.n_kv_heads)
+
+
+def cpu_stream(wl, seed, i, L, sm):
+    """Oracle seconds for stream i (sequence i // Hkv, kv head i % Hkv) of one layer: the
+    new token's quantization and the decode attention of every query head of its group
+    over all L + 1 tokens (the prefix quantization is not timed)."""
     import numpy as np
 
     import oracle
     import synth
 
+    b, h = divmod(i, wl.n_kv_heads)
     ks = synth.key_scale(seed, wl)
     cbk, cbv = synth.codebook(seed, wl.k_bits, "k"), synth.codebook(seed, wl.v_bits, "v")
     q = synth.queries(seed, wl)
-    elapsed = 0.0
-    for h in range(n_heads):
-        kx = synth.keys(seed, wl, 0, h, L + 1).numpy()
-        vx = synth.values(seed, wl, 0, h, L + 1).numpy()
-        cache = oracle.quantize_stream(kx[:L], vx[:L], ks[h], cbk, cbv, wl.n_outliers)  # prefix: not timed
-        t0 = time.perf_counter()
-        new = oracle.quantize_stream(kx[L:], vx[L:], ks[h], cbk, cbv, wl.n_outliers)
-        full = oracle.StreamCache(*(np.concatenate([a, b]) for a, b in zip(
-            (cache.k_codes, cache.k_idx, cache.k_val, cache.v_codes, cache.v_idx, cache.v_val, cache.v_scale),
-            (new.k_codes, new.k_idx, new.k_val, new.v_codes, new.v_idx, new.v_val, new.v_scale))))
-        oracle.pack_key_records(new.k_codes, wl.k_bits)
-        for hq in range(h * wl.group, (h + 1) * wl.group):
-            oracle.decode_head(q[0, hq].float().numpy().astype(np.float64), full, ks[h], cbk, cbv,
-                               wl.rope_base, sm)
-        elapsed += time.perf_counter() - t0
-    return elapsed
+    kx = synth.keys(seed, wl, b, h, L + 1).numpy()
+    vx = synth.values(seed, wl, b, h, L + 1).numpy()
+    cache = oracle.quantize_stream(kx[:L], vx[:L], ks[h], cbk, cbv, wl.n_outliers)  # prefix: not timed
+    t0 = time.perf_counter()
+    new = oracle.quantize_stream(kx[L:], vx[L:], ks[h], cbk, cbv, wl.n_outliers)
+    full = oracle.StreamCache(*(np.concatenate([a, b]) for a, b in zip(
+        (cache.k_codes, cache.k_idx, cache.k_val, cache.v_codes, cache.v_idx, cache.v_val, cache.v_scale),
+        (new.k_codes, new.k_idx, new.k_val, new.v_codes, new.v_idx, new.v_val, new.v_scale))))
+    oracle.pack_key_records(new.k_codes, wl.k_bits)
+    for hq in range(h * wl.group, (h + 1) * wl.group):
+        oracle.decode_head(q[b, hq].float().numpy().astype(np.float64), full, ks[h], cbk, cbv, wl.rope_base, sm)
+    return time.perf_counter() - t0
 
 
 def key_scale_leg(wl, cfg, seed):
@@ -479,8 +529,13 @@ def main():
         torch.cuda.synchronize()
         del src_p, dst_p
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.seed * 1000, min(args.cpu_heads, wl.batch * wl.n_kv_heads),
-                                            args.cpu_layers)
+        n_streams = min(args.cpu_heads, wl.batch * wl.n_kv_heads)
+        line["cpu_baseline"] = cpu_baseline(wl, args.seed * 1000, n_streams, args.cpu_layers)
+        # the machine's CPU share is 16 threads per GPU, whatever the host reports
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        if workers > 1:
+            line["cpu_baseline_parallel"] = cpu_baseline_parallel(wl, args.seed * 1000, n_streams, args.cpu_layers,
+                                                                  workers)
     print(json.dumps(line), flush=True)
 
 
