@@ -54,6 +54,38 @@ def select_outliers(x16, k: int) -> np.ndarray:
     return np.sort(order[:, :k], axis=1)
 
 
+# Channel index of an unused outlier slot (key vectors under the per-channel rule).
+NO_OUTLIER = 255
+
+
+def select_outliers_by_threshold(x16, k_scale32, k: int):
+    """Key outliers under the per-channel reading of [P1 (iv)]: keys are quantized per
+    channel [P1 (i); P2 item (1)], so a key entry counts as an outlier by its own
+    channel's standard, the frozen per-channel scale s_c, which then also bounds every
+    dense entry it leaves.
+
+    Entry c of a vector is a candidate iff |x_c| > s_c (float32 comparison).  A vector
+    keeps at most ``k`` candidates: those with the largest float32 ratio |x_c| / s_c
+    (+inf where s_c = 0), ties toward the lower channel; candidates beyond k stay dense.
+    Returns (idx int64 [N, k]: the kept channels in ascending order, then NO_OUTLIER in
+    the unused slots; count int64 [N])."""
+    x = _as_f16(x16)
+    n, d = x.shape
+    idx = np.full((n, k), NO_OUTLIER, dtype=np.int64)
+    count = np.zeros(n, dtype=np.int64)
+    if k == 0:
+        return idx, count
+    mag = np.abs(x.astype(np.float32))
+    s = np.asarray(k_scale32, dtype=np.float32)
+    for r in range(n):
+        cand = [c for c in range(d) if mag[r, c] > s[c]]
+        ratio = {c: (np.float32(mag[r, c] / s[c]) if s[c] > 0 else np.float32(np.inf)) for c in cand}
+        kept = sorted(sorted(cand, key=lambda c: (-float(ratio[c]), c))[:k])
+        idx[r, :len(kept)] = kept
+        count[r] = len(kept)
+    return idx, count
+
+
 def nearest_code(u32: np.ndarray, codebook32: np.ndarray) -> np.ndarray:
     """Non-uniform code assignment [P1 (iii); P2 item (3)].
 
@@ -73,11 +105,11 @@ def nearest_code(u32: np.ndarray, codebook32: np.ndarray) -> np.ndarray:
 
 def _dense_part(x16, idx) -> np.ndarray:
     """x with its outlier entries set to zero, as float32 (the dense half of the
-    dense-and-sparse split x = dense + sparse)."""
+    dense-and-sparse split x = dense + sparse); NO_OUTLIER slots are skipped."""
     d = _as_f16(x16).astype(np.float32).copy()
-    rows = np.arange(d.shape[0])[:, None]
-    if idx.shape[1]:
-        d[rows, idx] = 0.0
+    idx = np.asarray(idx, np.int64)
+    r, j = np.nonzero(idx != NO_OUTLIER)
+    d[r, idx[r, j]] = 0.0
     return d
 
 
@@ -89,23 +121,31 @@ def _normalise(d32: np.ndarray, s32: np.ndarray) -> np.ndarray:
     return np.where(s > 0, u, np.float32(0.0)).astype(np.float32)
 
 
-def quantize_keys(x16, k_scale32, codebook32, k: int):
+def quantize_keys(x16, k_scale32, codebook32, k: int, per_channel: bool = False):
     """Quantize key vectors of one kv head, pre-RoPE, with a per-channel scale.
 
     [P1 (i), (ii), (iii), (iv); P2 items (1)-(4)]
-      x16        fp16 [N, D] pre-RoPE keys
-      k_scale32  float32 [D]: this kv head's frozen per-channel scale
-      codebook32 float32 [2^b], ascending, the layer's key codebook
+      x16         fp16 [N, D] pre-RoPE keys
+      k_scale32   float32 [D]: this kv head's frozen per-channel scale
+      codebook32  float32 [2^b], ascending, the layer's key codebook
+      per_channel False: each vector's k largest |x_c| are its outliers
+                  (select_outliers); True: the per-channel rule
+                  (select_outliers_by_threshold), unused slots NO_OUTLIER with value 0
     Returns (codes uint8 [N, D], out_idx uint8 [N, k], out_val uint16 [N, k]).
     The dense part (outliers zeroed) is divided channel-wise by the scale and mapped
     to the nearest code; outliers keep their fp16 bits unchanged."""
     x = _as_f16(x16)
-    idx = select_outliers(x, k)
+    if per_channel:
+        idx = select_outliers_by_threshold(x, k_scale32, k)[0]
+    else:
+        idx = select_outliers(x, k)
     d = _dense_part(x, idx)
     u = _normalise(d, np.asarray(k_scale32, dtype=np.float32)[None, :])
     codes = nearest_code(u, codebook32)
     rows = np.arange(x.shape[0])[:, None]
-    val = x.view(np.uint16)[rows, idx] if k else np.zeros((x.shape[0], 0), np.uint16)
+    used = idx != NO_OUTLIER
+    val = x.view(np.uint16)[rows, np.where(used, idx, 0)] if k else np.zeros((x.shape[0], 0), np.uint16)
+    val = np.where(used, val, np.uint16(0))
     return codes, idx.astype(np.uint8), np.ascontiguousarray(val, dtype=np.uint16)
 
 
@@ -207,9 +247,11 @@ def unpack_value_tiles(tiles: np.ndarray, bits: int, d: int, n: int) -> np.ndarr
 
 
 def _scatter_outliers(x: np.ndarray, idx, val) -> np.ndarray:
-    if np.asarray(idx).shape[-1]:
-        rows = np.arange(x.shape[0])[:, None]
-        x[rows, np.asarray(idx, np.int64)] = np.asarray(val, np.uint16).view(np.float16).astype(np.float64)
+    """Outlier channels take their stored fp16 value; NO_OUTLIER slots change nothing."""
+    idx = np.asarray(idx, np.int64)
+    v = np.asarray(val, np.uint16).view(np.float16).astype(np.float64)
+    r, j = np.nonzero(idx != NO_OUTLIER)
+    x[r, idx[r, j]] = v[r, j]
     return x
 
 
@@ -287,8 +329,10 @@ class StreamCache:
         return self.k_codes.shape[0]
 
 
-def quantize_stream(k16, v16, k_scale32, k_codebook32, v_codebook32, k: int) -> StreamCache:
-    kc, ki, kv = quantize_keys(k16, k_scale32, k_codebook32, k)
+def quantize_stream(k16, v16, k_scale32, k_codebook32, v_codebook32, k: int,
+                    per_channel_keys: bool = False) -> StreamCache:
+    """Keys and values of one stream; per_channel_keys selects the keys' outlier rule."""
+    kc, ki, kv = quantize_keys(k16, k_scale32, k_codebook32, k, per_channel_keys)
     vc, vi, vv, vs = quantize_values(v16, v_codebook32, k)
     return StreamCache(kc, ki, kv, vc, vi, vv, vs)
 

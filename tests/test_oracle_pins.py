@@ -428,3 +428,78 @@ def test_key_scale_is_the_channel_max_of_the_dense_part():
                     exp[c] = max(exp[c], abs(float(x[t, c])))
         assert np.array_equal(got.astype(np.float64), exp), k
     assert np.array_equal(oracle.key_scale_from_keys(x, 16), np.zeros(16, np.float32))
+
+
+# ---- per-channel key outliers (candidates |x_c| > s_c, at most k, largest |x_c|/s_c) ----
+
+def test_per_channel_rule_properties_on_many_vectors():
+    """Checked against what the rule must satisfy, not a restatement of it: every kept
+    channel exceeds its scale; the count is min(#candidates, k); no dropped candidate beats
+    a kept one in (ratio, -channel) order; kept channels ascend, unused slots hold the
+    sentinel; the dense part then lies in [-s_c, s_c] outside the dropped candidates."""
+    rng = np.random.default_rng(11)
+    x = rng.choice(np.float16([-6, -3, -2, -1, -0.5, 0, 0.5, 1, 2, 3, 6]), size=(200, D)).astype(np.float16)
+    s = rng.choice(np.float32([0.0, 0.5, 1.0, 2.0, 3.0, 4.0]), size=D).astype(np.float32)
+    for k in (0, 1, 2, 4, D):
+        idx, count = oracle.select_outliers_by_threshold(x, s, k)
+        for r in range(x.shape[0]):
+            mag = [abs(float(x[r, c])) for c in range(D)]
+            cand = [c for c in range(D) if mag[c] > s[c]]
+            kept = [int(c) for c in idx[r] if c != oracle.NO_OUTLIER]
+            assert count[r] == len(kept) == min(len(cand), k)
+            assert kept == sorted(kept) and all(c in cand for c in kept)
+            assert all(c == oracle.NO_OUTLIER for c in idx[r][len(kept):])
+            ratio = lambda c: Fraction(mag[c]) / Fraction(float(s[c])) if s[c] > 0 else math.inf
+            for c in cand:
+                if c in kept:
+                    continue
+                for kc in kept:  # a dropped candidate never outranks a kept one
+                    assert (ratio(kc), -kc) > (ratio(c), -c)
+
+
+def test_per_channel_rule_reduces_to_top_k_for_a_uniform_power_of_two_threshold():
+    """With the same power-of-two scale below every |x_c| in every channel, |x_c|/s orders
+    exactly like |x_c|: the rule is the per-vector top-k rule."""
+    rng = np.random.default_rng(5)
+    x = (rng.choice(np.float16([1, 2, 3, 4, 5, 6, 7, 8]), size=(100, D)) *
+         rng.choice(np.float16([-1, 1]), size=(100, D))).astype(np.float16)
+    s = np.full(D, 0.5, np.float32)
+    for k in (1, 2, 5):
+        idx, count = oracle.select_outliers_by_threshold(x, s, k)
+        assert np.all(count == k)
+        assert np.array_equal(idx, oracle.select_outliers(x, k))
+
+
+def test_per_channel_keys_decode_and_sentinel_slots():
+    """Unused slots (sentinel channel, value 0) change nothing when decoding; kept outliers
+    decode exactly; dense entries are within the quantizer's error bound of x; a candidate
+    dropped by the cap lands on an end code."""
+    cb = synth.uniform_codebook(3)
+    x = np.zeros((2, D), np.float16)
+    s = np.ones(D, np.float32)
+    x[0, 3], x[0, 70], x[0, 9] = 5.0, -7.0, 0.75   # two candidates, k = 4 -> two sentinels
+    x[1, [1, 2, 3]] = [9.0, 4.0, 2.0]               # three candidates, k = 2 -> channel 3 stays dense
+    codes, idx, val = oracle.quantize_keys(x, s, cb, 4, per_channel=True)
+    assert list(idx[0]) == [3, 70, oracle.NO_OUTLIER, oracle.NO_OUTLIER] and list(val[0][2:]) == [0, 0]
+    deq = oracle.dequant_keys(codes, idx, val, s, cb)
+    assert deq[0, 3] == 5.0 and deq[0, 70] == -7.0
+    assert abs(deq[0, 9] - 0.75) <= (2.0 / 7) / 2 + 1e-12
+    codes2, idx2, val2 = oracle.quantize_keys(x, s, cb, 2, per_channel=True)
+    assert list(idx2[1]) == [1, 2]
+    assert codes2[1, 3] == len(cb) - 1  # u = 2 clamps to the top entry
+    # the same codes with the sentinel slots removed decode identically
+    assert np.array_equal(oracle.dequant_keys(codes, idx[:, :2], val[:, :2], s, cb)[0], deq[0])
+
+
+def test_per_channel_keys_with_all_entries_outliers_is_exact_attention():
+    """k = D and tiny scales: every nonzero entry is an outlier, so the keys decode exactly
+    and attention equals exact attention over the fp16 keys."""
+    rng = np.random.default_rng(2)
+    n = 40
+    k16 = rng.standard_normal((n, D)).astype(np.float16)
+    v16 = rng.standard_normal((n, D)).astype(np.float16)
+    s = np.full(D, 1e-30, np.float32)
+    c = oracle.quantize_stream(k16, v16, s, synth.uniform_codebook(2), synth.uniform_codebook(2), D,
+                               per_channel_keys=True)
+    kd = oracle.dequant_keys(c.k_codes, c.k_idx, c.k_val, s, synth.uniform_codebook(2))
+    assert np.array_equal(kd, k16.astype(np.float64))
