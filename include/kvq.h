@@ -76,6 +76,17 @@ typedef struct {
   int32_t v_bits;      /* 2, 3 or 4 */
   int32_t n_outliers;  /* k per (token, kv head) vector, 0 <= k <= D */
   float rope_base;     /* rotary base (10000 for LLaMA-family models), > 1 */
+  int32_t key_outliers; /* rule choosing each key vector's outliers (values always use 0):
+                           0  per vector: its k largest |x_c| (ties to the lower channel);
+                           1  per channel (keys are quantized per channel): the candidates
+                              |x_c| > k_scale[c] (so the dense part stays within its
+                              channel's scale), at most k of them, largest float32
+                              |x_c| / k_scale[c] first (+inf where the scale is 0), ties to
+                              the lower channel; unused slots hold channel 255 and value 0.
+                           The pages quantize keys per channel and isolate outliers per
+                           vector (summary page, techniques (i) and (iv); paper note, items
+                           (1) and (4)) without fixing whose standard makes an outlier; 1
+                           is the per-channel reading.  Other values: KVQ_ERR_INVALID. */
 } kvq_shape;
 
 typedef struct {
@@ -118,10 +129,12 @@ size_t kvq_workspace_bytes(const kvq_shape* shape, int32_t max_len);
  *                  capacity then: a sequence without room for its new tokens appends
  *                  nothing and keeps its length (visible in seq_len).  Requires
  *                  n_kv_heads <= 127.
- * Per new vector: the k largest |x| entries (ties to the lower channel) go to the outlier
- * store in ascending channel order with their fp16 bits; the dense rest (outlier slots
- * zeroed) is divided in float32 by the key's per-channel scale or by the value vector's
- * own max |dense| (0 -> all-zero u) and coded as the lowest j minimising |u - cb_j|.
+ * Per new vector: its outliers (values and, with key_outliers = 0, keys: the k largest
+ * |x| entries, ties to the lower channel; keys with key_outliers = 1: the per-channel rule
+ * of kvq_shape) go to the outlier store in ascending channel order with their fp16 bits;
+ * the dense rest (outlier slots zeroed) is divided in float32 by the key's per-channel
+ * scale or by the value vector's own max |dense| (0 -> all-zero u) and coded as the lowest
+ * j minimising |u - cb_j| (a key entry beyond its scale lands on an end code).
  * Afterwards seq_len[b] = old length + n_new (device), enqueued on `stream`.
  * Errors: KVQ_ERR_CAPACITY if any seq_len_host[b] + n_new > max_seq (host positions).
  * Calls that overlap on one cache (e.g. on two streams) race.
@@ -234,7 +247,7 @@ const char* kvq_status_string(int status);
 /* ABI version of this header (bumped on any incompatible change). */
 int kvq_abi_version(void);
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ EXPORTED = ("kvq_cache_sizes", "kvq_workspace_bytes", "kvq_quantize_append", "kv
             "kvq_pv_matvec", "kvq_decode_attention", "kvq_key_scale", "kvq_fit_workspace_bytes", "kvq_fit_codebook",
             "kvq_fp16_qk_matvec", "kvq_fp16_pv_matvec", "kvq_status_string",
             "kvq_abi_version")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class KvqError(RuntimeError):
@@ -38,7 +38,7 @@ class Shape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("max_seq", ctypes.c_int32), ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32),
-                ("n_outliers", ctypes.c_int32), ("rope_base", ctypes.c_float)]
+                ("n_outliers", ctypes.c_int32), ("rope_base", ctypes.c_float), ("key_outliers", ctypes.c_int32)]
 
 
 class CacheDesc(ctypes.Structure):
@@ -128,10 +128,11 @@ class CacheConfig:
     n_outliers: int
     head_dim: int = 128
     rope_base: float = 10000.0
+    key_outliers: int = 0  # 0: per vector (k largest |x|); 1: per channel (|x_c| > k_scale[c], at most k)
 
     def shape(self) -> Shape:
         return Shape(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim, self.max_seq,
-                     self.k_bits, self.v_bits, self.n_outliers, self.rope_base)
+                     self.k_bits, self.v_bits, self.n_outliers, self.rope_base, self.key_outliers)
 
 
 def cache_sizes(cfg: CacheConfig) -> Sizes:

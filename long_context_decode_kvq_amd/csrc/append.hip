@@ -114,7 +114,10 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
         const uint32_t x0 = use_pre ? pre0 : a.k_new[src + lane];
         const uint32_t x1 = use_pre ? pre1 : a.k_new[src + lane + kHalf];
         bool sel0, sel1;
-        select_outliers(outlier_key(x0, lane), outlier_key(x1, lane + kHalf), k, sel0, sel1);
+        if (a.key_per_channel)  // launch-uniform
+          select_outliers_by_scale(x0, x1, ks0, ks1, lane, k, sel0, sel1);
+        else
+          select_outliers(outlier_key(x0, lane), outlier_key(x1, lane + kHalf), k, sel0, sel1);
         const uint64_t b0 = __ballot(sel0);
         const uint64_t b1 = __ballot(sel1);
         if (sel0) {
@@ -126,6 +129,11 @@ __global__ __launch_bounds__(128) void append_kernel(AppendArgs a) {
           const int r = __popcll(b0) + __popcll(b1 & lt);
           a.k_idx[slot * k + r] = static_cast<uint8_t>(lane + kHalf);
           a.k_val[slot * k + r] = static_cast<uint16_t>(x1);
+        }
+        // slots past the kept outliers (per-channel rule only): the sentinel channel, value 0
+        for (int r = __popcll(b0) + __popcll(b1) + lane; r < k; r += kWave) {
+          a.k_idx[slot * k + r] = static_cast<uint8_t>(kNoOutlier);
+          a.k_val[slot * k + r] = 0;
         }
         const float d0 = sel0 ? 0.0f : half_bits_to_float(x0);
         const float d1 = sel1 ? 0.0f : half_bits_to_float(x1);

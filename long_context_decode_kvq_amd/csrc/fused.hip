@@ -270,9 +270,10 @@ __global__ __launch_bounds__(kFuseThreads) void fused_decode_kernel(QkArgs a, Pv
     // Key outliers: replace the decoded zero code zc * s_c at the channel by the stored
     // fp16 value, at the channel's rotated query coefficient.
     auto add_outlier = [&](uint32_t c, uint32_t vbits) {
-      c &= kHeadDim - 1;  // a token past the length may hold stale bytes
+      const bool used = c != kNoOutlier;  // an unused slot (per-channel rule) adds nothing
+      c &= kHeadDim - 1;                  // a token past the length may hold stale bytes
       const int i = c & (kHalf - 1);
-      const float dv = half_bits_to_float(vbits) - zc * ks[c];
+      const float dv = used ? half_bits_to_float(vbits) - zc * ks[c] : 0.0f;
       const float2 th = thl[i];
       const float ph = fmaf(tauf, th.y, __builtin_amdgcn_fractf(tauf * th.x));
       const float cs = __builtin_amdgcn_cosf(ph), sn = __builtin_amdgcn_sinf(ph);

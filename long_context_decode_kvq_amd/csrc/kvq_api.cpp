@@ -26,6 +26,7 @@ int check_shape(const kvq_shape* s) {
   if (s->n_outliers > s->head_dim) return KVQ_ERR_INVALID;
   if (!bits_ok(s->k_bits) || !bits_ok(s->v_bits)) return KVQ_ERR_UNSUPPORTED;
   if (!group_ok(s->n_q_heads / s->n_kv_heads)) return KVQ_ERR_UNSUPPORTED;
+  if (s->key_outliers != 0 && s->key_outliers != 1) return KVQ_ERR_INVALID;
   return KVQ_OK;
 }
 
@@ -192,6 +193,7 @@ int kvq_quantize_append(const kvq_shape* s, const kvq_cache* c, const uint16_t* 
     a.n_max = n_max;
     a.n_batch = nb;
     a.device_positions = device_positions ? 1 : 0;
+    a.key_per_channel = s->key_outliers;
     a.k_new = k_new ? k_new + static_cast<size_t>(b0) * n_max * H * D : nullptr;
     a.v_new = v_new ? v_new + static_cast<size_t>(b0) * n_max * H * D : nullptr;
     a.k_codes = c->k_codes + slot0 * D * s->k_bits / 8;

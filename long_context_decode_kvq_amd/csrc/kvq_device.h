@@ -196,6 +196,34 @@ __device__ __forceinline__ void select_outliers(uint32_t key0, uint32_t key1, in
   }
 }
 
+// Per-channel key outliers: channel c (fp16 bits x, frozen scale s >= 0) is a candidate
+// iff |x| > s; the wave keeps at most k, the largest float32 |x| / s first (+inf where
+// s = 0), ties toward the lower channel.  Lane l holds channels l (x0, s0) and l + 64
+// (x1, s1).  A candidate's ratio is positive, so its bits order as unsigned integers.
+__device__ __forceinline__ void select_outliers_by_scale(uint32_t x0, uint32_t x1, float s0, float s1, int lane,
+                                                         int k, bool& sel0, bool& sel1) {
+  const float m0 = fabsf(half_bits_to_float(x0)), m1 = fabsf(half_bits_to_float(x1));
+  const uint32_t r0 = m0 > s0 ? __builtin_bit_cast(uint32_t, s0 > 0.0f ? m0 / s0 : INFINITY) : 0u;
+  const uint32_t r1 = m1 > s1 ? __builtin_bit_cast(uint32_t, s1 > 0.0f ? m1 / s1 : INFINITY) : 0u;
+  sel0 = false;
+  sel1 = false;
+  for (int r = 0; r < k; ++r) {
+    const uint32_t e0 = sel0 ? 0u : r0, e1 = sel1 ? 0u : r1;
+    const uint32_t best = wave_max_u32(e0 > e1 ? e0 : e1);
+    if (best == 0u) break;  // no candidate left (wave-uniform)
+    const uint32_t ch = e0 == best ? static_cast<uint32_t>(lane) : e1 == best ? static_cast<uint32_t>(lane + 64) : 255u;
+    const uint32_t lowest = ~wave_max_u32(~ch);  // wave minimum
+    if (lowest == static_cast<uint32_t>(lane)) {
+      sel0 = true;
+    } else if (lowest == static_cast<uint32_t>(lane + 64)) {
+      sel1 = true;
+    }
+  }
+}
+
+// Channel index of an unused key-outlier slot (per-channel rule): it adds nothing.
+constexpr uint32_t kNoOutlier = 255;
+
 // LDS byte address of a pointer into shared memory.
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(p)));

@@ -15,6 +15,7 @@ constexpr int kMaxKvHeadsDevicePos = 127;     // arrival counter width of a devi
 struct AppendArgs {
   int32_t n_kv_heads, max_seq, n_outliers, n_max, n_batch;  // n_batch: sequences in this launch
   int32_t device_positions;  // 1: start positions come from seq_len on the device
+  int32_t key_per_channel;   // 1: key outliers by the per-channel rule (|x_c| > s_c, at most k)
   const uint16_t* k_new;  // [n_batch][n_max][Hkv][D] (already offset to the first sequence)
   const uint16_t* v_new;
   uint8_t* k_codes;  // cache buffers offset to the first sequence of this launch

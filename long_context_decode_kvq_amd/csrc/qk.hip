@@ -351,8 +351,9 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
     // Outliers: the record holds the zero code at each outlier channel; replace its
     // decoded value zc * s_c by the stored fp16 value.
     auto add_outlier = [&](int c, uint32_t vbits) {
-      c &= kHeadDim - 1;  // a token past the length may hold stale bytes
-      const float dv = half_bits_to_float(vbits) - zc * ks[c];
+      const bool used = c != static_cast<int>(kNoOutlier);  // an unused slot (per-channel rule) adds nothing
+      c &= kHeadDim - 1;                                     // a token past the length may hold stale bytes
+      const float dv = used ? half_bits_to_float(vbits) - zc * ks[c] : 0.0f;
       const int i = c & (kHalf - 1);
       const float2 e = et[i][lane];
       const bool upper = c >= kHalf;

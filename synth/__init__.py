@@ -161,15 +161,21 @@ def queries(seed: int, wl: Workload, device="cpu") -> torch.Tensor:
     return t.to(device)
 
 
-def key_scale(seed: int, wl: Workload, n_calib: int = 4096) -> np.ndarray:
-    """Frozen per-channel key scale [n_kv_heads, head_dim] float32: the largest raw
-    |key| per channel over a separately seeded calibration draw of ``n_calib`` tokens.
-    Tokens seen later may exceed it; they then land on an end code."""
+def key_scale(seed: int, wl: Workload, n_calib: int = 4096, quantile: float | None = None) -> np.ndarray:
+    """Frozen per-channel key scale [n_kv_heads, head_dim] float32 from a separately
+    seeded calibration draw of ``n_calib`` tokens: the largest raw |key| per channel
+    (``quantile`` None; tokens seen later may exceed it and then land on an end code),
+    or the ``quantile`` of |key| per channel (linear interpolation in float64, rounded
+    to float32), a threshold that about a 1 - quantile share of entries exceed."""
     out = np.zeros((wl.n_kv_heads, wl.head_dim), dtype=np.float32)
     for h in range(wl.n_kv_heads):
         gen = _torch_gen("cpu", "calib", seed, wl.name, wl.key_tail, h)
         x = _key_draw(gen, n_calib, wl, scaled_channels(seed, wl, h), "cpu")
-        out[h] = x.float().abs().amax(dim=0).numpy()
+        a = x.float().abs()
+        if quantile is None:
+            out[h] = a.amax(dim=0).numpy()
+        else:
+            out[h] = np.quantile(a.numpy().astype(np.float64), quantile, axis=0).astype(np.float32)
     return out
 
 

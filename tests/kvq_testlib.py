@@ -40,8 +40,9 @@ class Case:
     """One seeded workload instance: the oracle's view and (optionally) the GPU cache."""
 
     def __init__(self, wl: synth.Workload, seed: int = 0, lens=None, device="cpu", max_seq=None,
-                 k_codebook=None, v_codebook=None, k_scale=None):
+                 k_codebook=None, v_codebook=None, k_scale=None, key_outliers=0):
         self.wl, self.seed, self.device = wl, seed, device
+        self.key_outliers = key_outliers  # 0: per-vector top-k; 1: per-channel thresholds
         self.lens = np.asarray(synth.seq_lens(wl) if lens is None else lens, dtype=np.int64)
         need = int(self.lens.max())
         self.max_seq = max_seq or max(64, ((need + 63) // 64) * 64)
@@ -58,7 +59,8 @@ class Case:
         if (b, h) not in self._oracle:
             ks, vs = self.streams[(b, h)]
             self._oracle[(b, h)] = oracle.quantize_stream(ks.cpu().numpy(), vs.cpu().numpy(), self.ks[h],
-                                                          self.cbk, self.cbv, self.k)
+                                                          self.cbk, self.cbv, self.k,
+                                                          per_channel_keys=self.key_outliers == 1)
         return self._oracle[(b, h)]
 
     def q_head(self, b, hq) -> np.ndarray:
@@ -78,7 +80,7 @@ class Case:
         import long_context_decode_kvq_amd as kvq
         wl = self.wl
         cfg = kvq.CacheConfig(wl.batch, wl.n_q_heads, wl.n_kv_heads, self.max_seq, wl.k_bits, wl.v_bits,
-                              self.k, D, wl.rope_base)
+                              self.k, D, wl.rope_base, self.key_outliers)
         cache = kvq.KVCache(cfg, torch.from_numpy(self.ks), torch.from_numpy(self.cbk),
                             torch.from_numpy(self.cbv), device=self.device)
         target = self.lens if upto is None else np.asarray(upto, dtype=np.int64)

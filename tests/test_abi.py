@@ -67,7 +67,7 @@ def test_workspace_bytes():
 @pytest.mark.parametrize("field,value,status", [
     ("head_dim", 64, -2), ("k_bits", 5, -2), ("v_bits", 1, -2), ("n_q_heads", 6, -2),
     ("max_seq", 100, -1), ("n_outliers", 129, -1), ("n_outliers", -1, -1), ("batch", 0, -1),
-    ("rope_base", 0.5, -1)])
+    ("rope_base", 0.5, -1), ("key_outliers", 2, -1), ("key_outliers", -1, -1)])
 def test_bad_shapes_rejected(field, value, status):
     c = cfg(**{field: value})
     out = kvq.Sizes()

@@ -8,8 +8,9 @@ outlier indices/values and value scales bit for bit over every token, and for ev
 query head of the stream's group every logit (|dl| <= 1e-3 sm sum_c |q_c y_c|) and the
 output (|do| <= 1e-3 sum_t p_t |v~_t|).  Sizes: the LLaMA-7B-shaped layer at 32K tokens
 (3-bit), 128K (4-bit, Laplace outlier channels) and 1M (2-bit), and the Llama-3-8B-shaped
-GQA layer (batch 16, 32 query heads on 8 kv heads, 64K tokens each); the oracle needs
-about a minute of host time for the 1M stream.
+GQA layer (batch 16, 32 query heads on 8 kv heads, 64K tokens each), and the 32K layer
+again under the per-channel key outlier rule; the oracle needs about a minute of host
+time for the 1M stream.
 """
 import math
 
@@ -31,20 +32,23 @@ SAMPLED = {
     "llama7b_128k_4bit": [(0, 5)],
     "llama7b_1m_2bit": [(0, 9)],
     "llama3_8b_gqa_b16_64k": [(0, 0), (9, 5), (15, 7)],
+    # the per-channel key outlier rule, each channel's scale the 0.99 quantile of |key|
+    "llama7b_32k@per_channel": [(0, 3), (0, 30)],
 }
 
 
 @pytest.mark.parametrize("name", sorted(SAMPLED))
 def test_full_layer_sampled_heads(name):
     import long_context_decode_kvq_amd as kvq
-    wl = synth.WORKLOADS[name]
+    per_channel = name.endswith("@per_channel")
+    wl = synth.WORKLOADS[name.split("@")[0]]
     seed = 0
     L0 = wl.seq_len
     n = L0 + 1  # the prompt plus one decode-step token
     S = ((n + 63) // 64) * 64
     cfg = kvq.CacheConfig(wl.batch, wl.n_q_heads, wl.n_kv_heads, S, wl.k_bits, wl.v_bits, wl.n_outliers, D,
-                          wl.rope_base)
-    ks = synth.key_scale(seed, wl)
+                          wl.rope_base, int(per_channel))
+    ks = synth.key_scale(seed, wl, quantile=0.99 if per_channel else None)
     cbk, cbv = synth.codebook(seed, wl.k_bits, "k"), synth.codebook(seed, wl.v_bits, "v")
     cache = kvq.KVCache(cfg, torch.from_numpy(ks), torch.from_numpy(cbk), torch.from_numpy(cbv), "cuda")
     kraw = torch.empty(wl.batch, n, wl.n_kv_heads, D, dtype=torch.float16, device="cuda")
@@ -71,7 +75,7 @@ def test_full_layer_sampled_heads(name):
     for b, h in SAMPLED[name]:
         k16 = kraw[b, :, h].cpu().numpy()
         v16 = vraw[b, :, h].cpu().numpy()
-        c = oracle.quantize_stream(k16, v16, ks[h], cbk, cbv, wl.n_outliers)
+        c = oracle.quantize_stream(k16, v16, ks[h], cbk, cbv, wl.n_outliers, per_channel_keys=per_channel)
         got = gpu_buffers(cache, b, h)
         what = f"{name} b={b} h={h}"
         assert np.array_equal(got["k_rec"][:n], oracle.pack_key_records(c.k_codes, wl.k_bits)), f"{what} k_rec"

@@ -50,13 +50,35 @@ CASES = {
     "mha2_2bit_k3": (_wl("llama7b_1m_2bit", n_q_heads=2, n_kv_heads=2, seq_len=1100, outlier_frac=0.02), [1100], None),
     "gqa4_k5_ragged": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=4, n_kv_heads=1, seq_len=900, outlier_frac=0.035),
                        [900, 333], None),
+    # the per-channel key outlier rule (key_outliers = 1): the frozen key scale is a
+    # per-channel quantile of |key| over the calibration draw and doubles as the threshold
+    "pc_mha4_3bit_k2": (_wl("llama7b_32k", n_q_heads=4, n_kv_heads=4, seq_len=1100), [1100], None),
+    "pc_mha2_3bit_k5": (_wl("llama7b_32k", n_q_heads=2, n_kv_heads=2, seq_len=1300, outlier_frac=0.035),
+                        [1300], None),
+    "pc_mha4_4bit_laplace": (_wl("llama7b_128k_4bit", n_q_heads=4, n_kv_heads=4, seq_len=1100), [1100], None),
+    "pc_mha2_2bit_capped": (_wl("llama7b_1m_2bit", n_q_heads=2, n_kv_heads=2, seq_len=900), [900], None),
+    "pc_gqa_incremental": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=8, n_kv_heads=2, seq_len=700),
+                           [700, 333], [1, 62, 1, 64, 65, 3, 200, 1, 400]),
+    "pc_k0": (_wl("llama7b_32k", n_q_heads=2, n_kv_heads=2, seq_len=500, outlier_frac=0.0), [500], None),
 }
+
+# per-channel cases -> the quantile of |key| taken as each channel's scale; 0.99 leaves about
+# 1.3 candidates per 128-entry vector (often more than k = 2), 0.5 about 64 (k always binds)
+PER_CHANNEL = {"pc_mha4_3bit_k2": 0.99, "pc_mha2_3bit_k5": 0.965, "pc_mha4_4bit_laplace": 0.99,
+               "pc_mha2_2bit_capped": 0.5, "pc_gqa_incremental": 0.99, "pc_k0": 0.99}
+
+
+def make_case(name, wl, lens, device="cuda", seed=3):
+    if name in PER_CHANNEL:
+        ks = synth.key_scale(seed, wl, quantile=PER_CHANNEL[name])
+        return Case(wl, seed=seed, lens=lens, device=device, k_scale=ks, key_outliers=1)
+    return Case(wl, seed=seed, lens=lens, device=device)
 
 
 @pytest.fixture(scope="module", params=sorted(CASES))
 def built(request):
     wl, lens, chunks = CASES[request.param]
-    case = Case(wl, seed=3, lens=lens, device="cuda")
+    case = make_case(request.param, wl, lens)
     cache = case.build_gpu(chunks)
     torch.cuda.synchronize()
     return request.param, case, cache
