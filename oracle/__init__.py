@@ -11,5 +11,5 @@ from .kvquant import (StreamCache, attend, decode_head, dequant_keys, dequant_va
                       output_tolerance_scale, pack_key_records, pack_value_tiles, qk_logits,
                       quantize_keys, quantize_stream, quantize_values, rope, rope_frequencies,
                       select_outliers, softmax, unpack_key_records, unpack_value_tiles,
-                      zero_code, key_scale_from_keys)
+                      zero_code, key_scale_from_keys, key_threshold_from_keys, exceed_budget)
 from .codebook_fit import clamp_inputs, finalize, fit_codebook, fit_init, fit_step, fixed_point, quantization_mse

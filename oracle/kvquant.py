@@ -23,6 +23,8 @@ value product are float64.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 # ----------------------------------------------------------------------------------
@@ -372,6 +374,37 @@ def output_tolerance_scale(logits, cache: StreamCache, v_codebook32, length: int
 # ----------------------------------------------------------------------------------
 # Key scale calibration
 # ----------------------------------------------------------------------------------
+
+
+def exceed_budget(outlier_frac: float, n: int) -> int:
+    """How many of a channel's n calibration entries may lie above its threshold:
+    floor(outlier_frac * n), the product formed in float64 (an IEEE double product,
+    then floor)."""
+    return int(math.floor(float(outlier_frac) * float(n)))
+
+
+def key_threshold_from_keys(k16, outlier_frac: float) -> np.ndarray:
+    """Per-channel key threshold for the per-channel outlier rule (R19 reading of
+    [P1 (i), (iv); P2 items (1), (4)]): the pages give no calibration for it, so the
+    threshold is the plainest one that keeps a chosen share of each channel's entries
+    out of range.  With N calibration vectors and m = exceed_budget(outlier_frac, N),
+    s_c is the smallest |x_c| of the calibration set that at most m entries of channel c
+    exceed, i.e. its (m+1)-th largest magnitude; 0 when m >= N (so also for N = 0).
+
+    Magnitudes are ordered as fp16 bit patterns with the sign cleared (numeric order for
+    finite numbers; a NaN ranks above +inf), and s_c is that fp16 magnitude as float32
+    (exact).  k16: [N, D] fp16 vectors of one kv head.  Returns float32 [D]."""
+    x = _as_f16(k16)
+    n, d = x.shape
+    m = exceed_budget(outlier_frac, n)
+    out = np.zeros(d, dtype=np.float32)
+    if m >= n:
+        return out
+    mag = (x.view(np.uint16) & np.uint16(0x7FFF)).astype(np.int64)
+    for c in range(d):
+        ordered = np.sort(mag[:, c])[::-1]           # largest first
+        out[c] = np.uint16(ordered[m]).view(np.float16).astype(np.float32)
+    return out
 
 
 def key_scale_from_keys(k16, k: int = 0) -> np.ndarray:

@@ -348,6 +348,18 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         test_nearest_code_matches_exact_rational_argmin(3)
     monkeypatch.setattr(oracle, "nearest_code", good_nc)
 
+    # 5. the key threshold's exceed budget off by one, or taken from a float32 fraction
+    good_budget = oracle.kvquant.exceed_budget
+    monkeypatch.setattr(oracle.kvquant, "exceed_budget", lambda f, n: good_budget(f, n) + 1)
+    with pytest.raises(AssertionError):
+        test_key_threshold_is_characterised_by_counting()
+    monkeypatch.setattr(oracle.kvquant, "exceed_budget", lambda f, n: int(math.floor(float(np.float32(f)) * n)))
+    monkeypatch.setattr(oracle, "exceed_budget", oracle.kvquant.exceed_budget)
+    with pytest.raises(AssertionError):
+        test_key_threshold_special_cases()
+    monkeypatch.setattr(oracle.kvquant, "exceed_budget", good_budget)
+    monkeypatch.setattr(oracle, "exceed_budget", good_budget)
+
 
 # ---- codebook fitting (unweighted k-means, oracle/codebook_fit.py) -----------------------
 
@@ -503,3 +515,57 @@ def test_per_channel_keys_with_all_entries_outliers_is_exact_attention():
                                per_channel_keys=True)
     kd = oracle.dequant_keys(c.k_codes, c.k_idx, c.k_val, s, synth.uniform_codebook(2))
     assert np.array_equal(kd, k16.astype(np.float64))
+
+
+# ---- per-channel key threshold (calibration for the per-channel outlier rule) ----------
+
+def test_key_threshold_golden_example():
+    """Hand-derived thresholds of a 5-vector, 4-channel example (tests/golden)."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "key_threshold_example.json")) as f:
+        g = json.load(f)
+    x = np.array(g["keys"], dtype=np.float16)
+    for case in g["cases"]:
+        assert oracle.exceed_budget(case["outlier_frac"], x.shape[0]) == case["m"], case
+        got = oracle.key_threshold_from_keys(x, case["outlier_frac"])
+        assert got.dtype == np.float32 and got.tolist() == case["threshold"], case
+
+
+def test_key_threshold_is_characterised_by_counting():
+    """Not a re-sort: s_c is a magnitude present in channel c, at most m entries lie above
+    it and at least m + 1 at or above it (so no smaller threshold keeps within m); s_c = 0
+    when m >= N.  Data with heavy ties, signed zeros and both signs."""
+    rng = np.random.default_rng(8)
+    vals = np.float16([0, -0.0, 0.25, -0.25, 1, -1, 1.5, 3, -3, 3, 7, 65504, -65504])
+    for n in (1, 2, 7, 64, 300):
+        x = rng.choice(vals, size=(n, 24)).astype(np.float16)
+        for f in (0.0, 0.001, 0.01, 0.1, 0.33, 0.5, 0.999, 1.0):
+            m = oracle.exceed_budget(f, n)
+            s = oracle.key_threshold_from_keys(x, f)
+            for c in range(24):
+                mag = [abs(float(v)) for v in x[:, c]]
+                if m >= n:
+                    assert s[c] == 0.0
+                    continue
+                above = sum(1 for a in mag if a > s[c])
+                at_or_above = sum(1 for a in mag if a >= s[c])
+                assert float(s[c]) in mag and above <= m < at_or_above, (n, f, c)
+
+
+def test_key_threshold_special_cases():
+    """f = 0 gives the channel maximum (the max-scale calibration without outliers); the
+    exceed budget is formed in float64 (0.01 of 300 is 3, where a float32 0.01 would
+    give 2); an empty calibration set gives zeros; the threshold does not depend on the
+    order of the vectors, and each channel only on its own entries."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((500, D)).astype(np.float16)
+    assert np.array_equal(oracle.key_threshold_from_keys(x, 0.0), oracle.key_scale_from_keys(x, 0))
+    assert oracle.exceed_budget(0.01, 300) == 3 and oracle.exceed_budget(0.5, 7) == 3
+    assert oracle.exceed_budget(1.0, 12345) == 12345
+    assert np.array_equal(oracle.key_threshold_from_keys(np.zeros((0, D), np.float16), 0.01), np.zeros(D, np.float32))
+    s = oracle.key_threshold_from_keys(x, 0.01)
+    perm_t, perm_c = rng.permutation(500), rng.permutation(D)
+    assert np.array_equal(oracle.key_threshold_from_keys(x[perm_t], 0.01), s)
+    assert np.array_equal(oracle.key_threshold_from_keys(x[:, perm_c], 0.01), s[perm_c])
+    # about 1 % of each channel's entries lie above its threshold
+    above = (np.abs(x.astype(np.float32)) > s).sum(axis=0)
+    assert np.all(above <= 5)
