@@ -242,8 +242,8 @@ def cpu_stream(wl, seed, i, L, sm):
 
 def key_scale_leg(wl, cfg, seed):
     """Per-channel key scale over a whole prompt of the workload (the keys a prefill
-    appends), each vector's outliers left out; returns the time and the bytes read per
-    second."""
+    appends), each vector's outliers left out, and the per-channel outlier threshold at a
+    1 % share over the same keys; returns each one's time and bytes read per second."""
     import torch
 
     import long_context_decode_kvq_amd as kvq
@@ -264,9 +264,21 @@ def key_scale_leg(wl, cfg, seed):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / 5
     nbytes = keys.numel() * 2
-    del keys
-    return {"tokens": wl.batch * n, "exclude_outliers": True, "ms": round(ms, 4),
-            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    # the per-channel outlier rule's threshold over the same prompt (two passes over the keys)
+    ws = torch.empty((kvq.key_threshold_workspace_bytes(cfg, n) + 3) // 4, dtype=torch.int32, device="cuda")
+    kvq.key_threshold(cfg, keys, 0.01, out, ws)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        kvq.key_threshold(cfg, keys, 0.01, out, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_t = e0.elapsed_time(e1) / 5
+    del keys, ws
+    return ({"tokens": wl.batch * n, "exclude_outliers": True, "ms": round(ms, 4),
+             "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)},
+            {"tokens": wl.batch * n, "outlier_frac": 0.01, "ms": round(ms_t, 4),
+             "gbs_per_pass": round(2 * nbytes / (ms_t * 1e-3) / 1e9, 1)})
 
 
 def codebook_fit_leg(wl, seed, iters=20, n_calib=4096):
@@ -518,7 +530,7 @@ def main():
         line["fused_single_pass"] = {"ms_per_layer": round(fms, 5), "two_call_ms_per_layer": round(kt["qk"] + kt["pv"], 5),
                                      "gbs": round((qk_bk + pv_bk - 8 * wl.batch * wl.n_q_heads * L_now) / (fms * 1e-3) / 1e9, 1)}
     if args.codebook_fit:
-        line["key_scale_calibration"] = key_scale_leg(wl, cfg, args.seed * 1000 + 7)
+        line["key_scale_calibration"], line["key_threshold_calibration"] = key_scale_leg(wl, cfg, args.seed * 1000 + 7)
         line["codebook_fit"] = codebook_fit_leg(wl, args.seed * 1000)
     if args.fp16_baseline:
         line["fp16_baseline"] = fp16_baseline(wl, cfg, L_now, args.kernel_steps, kt)

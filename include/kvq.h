@@ -198,6 +198,32 @@ int kvq_key_scale(const kvq_shape* shape, const uint16_t* keys, int32_t n_tokens
                   float* k_scale_out, hipStream_t stream);
 
 /*
+ * Per-channel key threshold for the per-channel outlier rule (key_outliers = 1), from a
+ * bulk of calibration keys, e.g. a prompt before its prefill append.  The pages quantize
+ * keys per channel and isolate outliers per vector (summary page, abstract paragraph,
+ * techniques (i) and (iv); paper note, items (1) and (4)) but give no calibration for a
+ * per-channel threshold; this one leaves a chosen share of each channel's calibration
+ * entries above it.  With N = B * n_tokens vectors and m = floor(outlier_frac * N) (the
+ * product in double precision), k_scale[h][c] = the (m+1)-th largest |x_c| over the
+ * vectors of kv head h, so at most m of them exceed it; 0 when m >= N (also for N = 0).
+ * Magnitudes are compared as fp16 bit patterns with the sign cleared (numeric order for
+ * finite keys; a NaN ranks above +inf); the result is that fp16 magnitude, exact.
+ *   keys              fp16 [B][n_tokens][Hkv][D], before the rotary embedding.
+ *   outlier_frac      share of entries allowed above the threshold, 0 <= f <= 1 (0 gives
+ *                     the channel maximum, as kvq_key_scale without exclusion).
+ *   k_scale_out       device float32 [Hkv][D]; overwritten.
+ *   workspace         device scratch of kvq_key_threshold_workspace_bytes(shape, n_tokens)
+ *                     bytes (NULL allowed when that is 0); its contents are not kept.
+ * Errors: KVQ_ERR_INVALID for f outside [0, 1] or NaN, n_tokens < 0, B * n_tokens >= 2^31,
+ * null pointers; KVQ_ERR_WORKSPACE for a missing or short workspace.  Six kernels are
+ * enqueued on `stream` (histograms of the magnitudes' high and low bits, their sums and
+ * the selections); calls sharing one workspace must not overlap.
+ */
+size_t kvq_key_threshold_workspace_bytes(const kvq_shape* shape, int32_t n_tokens);
+int kvq_key_threshold(const kvq_shape* shape, const uint16_t* keys, int32_t n_tokens, double outlier_frac,
+                      float* k_scale_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Per-layer codebook fitting (summary page, abstract paragraph, technique (iii); paper
  * note, item (3)): unweighted 1-D k-means over normalised calibration activations (keys
  * divided by their per-channel scale, values by their per-vector scale), the input of a
@@ -247,7 +273,7 @@ const char* kvq_status_string(int status);
 /* ABI version of this header (bumped on any incompatible change). */
 int kvq_abi_version(void);
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -22,10 +22,11 @@ KVQ_OK = 0
 STATUS_NAMES = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID", -2: "KVQ_ERR_UNSUPPORTED",
                 -3: "KVQ_ERR_CAPACITY", -4: "KVQ_ERR_WORKSPACE", -5: "KVQ_ERR_HIP"}
 EXPORTED = ("kvq_cache_sizes", "kvq_workspace_bytes", "kvq_quantize_append", "kvq_qk_matvec",
-            "kvq_pv_matvec", "kvq_decode_attention", "kvq_key_scale", "kvq_fit_workspace_bytes", "kvq_fit_codebook",
+            "kvq_pv_matvec", "kvq_decode_attention", "kvq_key_scale", "kvq_key_threshold_workspace_bytes",
+            "kvq_key_threshold", "kvq_fit_workspace_bytes", "kvq_fit_codebook",
             "kvq_fp16_qk_matvec", "kvq_fp16_pv_matvec", "kvq_status_string",
             "kvq_abi_version")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class KvqError(RuntimeError):
@@ -84,6 +85,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_decode_attention.restype = ctypes.c_int
     lib.kvq_key_scale.argtypes = [ctypes.POINTER(Shape), P, I32, I32, P, P]
     lib.kvq_key_scale.restype = ctypes.c_int
+    lib.kvq_key_threshold_workspace_bytes.argtypes = [ctypes.POINTER(Shape), I32]
+    lib.kvq_key_threshold_workspace_bytes.restype = SZ
+    lib.kvq_key_threshold.argtypes = [ctypes.POINTER(Shape), P, I32, ctypes.c_double, P, P, SZ, P]
+    lib.kvq_key_threshold.restype = ctypes.c_int
     lib.kvq_fit_workspace_bytes.argtypes = []
     lib.kvq_fit_workspace_bytes.restype = SZ
     lib.kvq_fit_codebook.argtypes = [P, ctypes.c_int64, I32, I32, P, P, SZ, P]
@@ -384,4 +389,28 @@ def key_scale(cfg: CacheConfig, keys: torch.Tensor, exclude_outliers: bool = Fal
     st = load_library().kvq_key_scale(ctypes.byref(cfg.shape()), keys.data_ptr() if keys.numel() else None,
                                       keys.shape[1], 1 if exclude_outliers else 0, out.data_ptr(), _stream(stream))
     _check("kvq_key_scale", st)
+    return out
+
+
+def key_threshold_workspace_bytes(cfg: CacheConfig, n_tokens: int) -> int:
+    return int(load_library().kvq_key_threshold_workspace_bytes(ctypes.byref(cfg.shape()), int(n_tokens)))
+
+
+def key_threshold(cfg: CacheConfig, keys: torch.Tensor, outlier_frac: float, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """kvq_key_threshold: calibration keys fp16 [B][n][Hkv][D] -> float32 [Hkv][D] per-channel
+    threshold for the per-channel outlier rule (the (m+1)-th largest |x_c|, m = floor(f N))."""
+    assert keys.dtype == torch.float16 and keys.is_contiguous() and keys.dim() == 4
+    assert keys.shape[0] == cfg.batch and keys.shape[2] == cfg.n_kv_heads and keys.shape[3] == cfg.head_dim
+    if out is None:
+        out = torch.empty(cfg.n_kv_heads, cfg.head_dim, dtype=torch.float32, device=keys.device)
+    need = key_threshold_workspace_bytes(cfg, keys.shape[1])
+    if workspace is None and need > 0:
+        workspace = torch.empty((need + 3) // 4, dtype=torch.int32, device=keys.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load_library().kvq_key_threshold(ctypes.byref(cfg.shape()), keys.data_ptr() if keys.numel() else None,
+                                          keys.shape[1], float(outlier_frac), out.data_ptr(), ws_ptr, ws_bytes,
+                                          _stream(stream))
+    _check("kvq_key_threshold", st)
     return out

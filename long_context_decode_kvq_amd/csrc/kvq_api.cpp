@@ -275,6 +275,28 @@ int kvq_key_scale(const kvq_shape* s, const uint16_t* keys, int32_t n_tokens, in
                                           exclude_outliers ? s->n_outliers : 0, k_scale_out, stream));
 }
 
+size_t kvq_key_threshold_workspace_bytes(const kvq_shape* s, int32_t n_tokens) {
+  if (check_shape(s) != KVQ_OK || n_tokens < 0) return 0;
+  if (static_cast<long long>(s->batch) * n_tokens >= (1LL << 31)) return 0;
+  return kvq::key_threshold_workspace_bytes(s->batch, n_tokens, s->n_kv_heads);
+}
+
+int kvq_key_threshold(const kvq_shape* s, const uint16_t* keys, int32_t n_tokens, double outlier_frac,
+                      float* k_scale_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_shape(s);
+  if (st != KVQ_OK) return st;
+  if (n_tokens < 0 || !k_scale_out || (n_tokens > 0 && !keys)) return KVQ_ERR_INVALID;
+  if (!(outlier_frac >= 0.0 && outlier_frac <= 1.0)) return KVQ_ERR_INVALID;  // NaN fails too
+  const long long n_vec = static_cast<long long>(s->batch) * n_tokens;
+  if (n_vec >= (1LL << 31)) return KVQ_ERR_INVALID;
+  const size_t need = kvq::key_threshold_workspace_bytes(s->batch, n_tokens, s->n_kv_heads);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return KVQ_ERR_WORKSPACE;
+  // the exceed budget floor(f N), the product formed in double precision
+  const long long budget = static_cast<long long>(std::floor(outlier_frac * static_cast<double>(n_vec)));
+  return hip_status(kvq::launch_key_threshold(keys, s->batch, n_tokens, s->n_kv_heads, budget, k_scale_out,
+                                              workspace, stream));
+}
+
 // ---- codebook fitting ---------------------------------------------------------------
 
 size_t kvq_fit_workspace_bytes(void) { return kvq::fit_workspace_bytes(); }

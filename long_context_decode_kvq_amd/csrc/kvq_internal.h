@@ -102,6 +102,11 @@ hipError_t launch_fp16_qk(int group, int batch, const Fp16Args& a, hipStream_t s
 // Per-channel key scale (max |x| over calibration keys, optionally their dense parts).
 hipError_t launch_key_scale(const uint16_t* keys, int batch, int n_tokens, int n_kv_heads, int k, float* out,
                             hipStream_t s);
+// Per-channel key threshold (the (budget+1)-th largest |x| per channel over calibration
+// keys, 0 when budget >= batch * n_tokens): workspace size and launcher.
+size_t key_threshold_workspace_bytes(int batch, int n_tokens, int n_kv_heads);
+hipError_t launch_key_threshold(const uint16_t* keys, int batch, int n_tokens, int n_kv_heads, long long budget,
+                                float* out, void* workspace, hipStream_t s);
 // Codebook fitting (k-means over normalised activations): workspace size and launcher.
 size_t fit_workspace_bytes();
 hipError_t launch_fit_codebook(int bits, const float* u, long long n, int iters, uint16_t* out, void* workspace,

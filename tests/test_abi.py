@@ -148,3 +148,29 @@ def test_key_scale_entry_point_rejects_before_launch():
     assert lib.kvq_key_scale(ctypes.byref(shape), p, 10, 2, p, None) == -1
     assert lib.kvq_key_scale(ctypes.byref(shape), p, 10, 0, None, None) == -1
     assert lib.kvq_key_scale(ctypes.byref(cfg(head_dim=64).shape()), p, 10, 0, p, None) == -2
+
+
+def test_key_threshold_entry_point_rejects_before_launch():
+    lib = kvq.load_library()
+    c = cfg()
+    shape = c.shape()
+    p = 4096
+    ws = lib.kvq_key_threshold_workspace_bytes(ctypes.byref(shape), 10)
+    assert ws > 0 and lib.kvq_key_threshold_workspace_bytes(ctypes.byref(shape), 0) == 0
+    assert lib.kvq_key_threshold_workspace_bytes(ctypes.byref(shape), -1) == 0
+    assert lib.kvq_key_threshold_workspace_bytes(ctypes.byref(shape), 2 ** 30) == 0  # 2 * 2^30 vectors
+    # 256 blocks' high-bit histograms (at least 64 vectors each), the summed ones, the selections
+    assert ws == 4 * (2 * 1 * 256 * 128 + 2 * 256 * 128) + 8 * 2 * 128
+    big = lib.kvq_key_threshold_workspace_bytes(ctypes.byref(shape), 1 << 20)
+    assert big == 4 * (2 * 128 * 256 * 128 + 2 * 256 * 128) + 8 * 2 * 128
+    T = lib.kvq_key_threshold
+    assert T(ctypes.byref(shape), None, 10, 0.01, p, p, ws, None) == -1          # no keys
+    assert T(ctypes.byref(shape), p, -1, 0.01, p, p, ws, None) == -1             # negative length
+    assert T(ctypes.byref(shape), p, 10, -0.1, p, p, ws, None) == -1             # fraction below 0
+    assert T(ctypes.byref(shape), p, 10, 1.5, p, p, ws, None) == -1              # fraction above 1
+    assert T(ctypes.byref(shape), p, 10, float("nan"), p, p, ws, None) == -1     # NaN fraction
+    assert T(ctypes.byref(shape), p, 10, 0.01, None, p, ws, None) == -1          # no output
+    assert T(ctypes.byref(shape), p, 2 ** 30, 0.01, p, p, ws, None) == -1        # 2^31 vectors
+    assert T(ctypes.byref(shape), p, 10, 0.01, p, None, ws, None) == -4          # no workspace
+    assert T(ctypes.byref(shape), p, 10, 0.01, p, p, ws - 1, None) == -4         # short workspace
+    assert T(ctypes.byref(cfg(head_dim=64).shape()), p, 10, 0.01, p, p, ws, None) == -2
