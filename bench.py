@@ -240,6 +240,28 @@ def cpu_stream(wl, seed, i, L, sm):
     return time.perf_counter() - t0
 
 
+def stream_ceiling(nbytes=1 << 30, reps=10):
+    """HBM read bandwidth of the library's plain streaming-read kernel over a 1 GiB buffer
+    (four times the last-level cache), the practical ceiling beside the 8 TB/s peak."""
+    import torch
+
+    import long_context_decode_kvq_amd as kvq
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kvq.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        kvq.stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del buf
+    return {"kernel": "kvq_stream_read", "bytes": nbytes, "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "pct_of_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
+
+
 def key_scale_leg(wl, cfg, seed):
     """Per-channel key scale over a whole prompt of the workload (the keys a prefill
     appends), each vector's outliers left out, and the per-channel outlier threshold at a
@@ -479,6 +501,34 @@ def main():
             fused_events.append((e0, e1))
         torch.cuda.synchronize()
 
+    # the decode step's append alone: every layer's device-positioned append of one token
+    # per sequence, back to back (the capacity holds these tokens too)
+    # per decode step (recorded once as a HIP graph when graphs are on, so the host's launch
+    # rate does not set the time of these short kernels)
+    def appends():
+        for j in range(args.kernel_steps):
+            for lay in layers:
+                kvq.quantize_append(lay["cache"], lay["new_k"][n_graph_steps + j], lay["new_v"][n_graph_steps + j],
+                                    device_positions=True)
+    e0, e1 = ev(), ev()
+    if args.graph:
+        g_app = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_app):
+            appends()
+        torch.cuda.synchronize()
+        e0.record()
+        g_app.replay()
+        e1.record()
+    else:
+        e0.record()
+        appends()
+        e1.record()
+    torch.cuda.synchronize()
+    app_events = [(e0, e1)]
+    for lay in layers:
+        lay["cache"].lengths = [x + wl.n_new * args.kernel_steps for x in lay["cache"].lengths]
+    ceiling = stream_ceiling()
+
     # bytes: lengths grow by n_new per step; use the mean length over the timed steps
     L_mean = start_len + wl.n_new * (args.steps + 1) / 2.0
     qk_b, pv_b, app_b = algorithmic_bytes(wl, L_mean)
@@ -519,6 +569,8 @@ def main():
         "kernel_ms": {k: round(v, 5) for k, v in kt.items()},
         "kernel_gbs": {"qk": round(qk_bk / (kt["qk"] * 1e-3) / 1e9, 1),
                        "pv": round(pv_bk / (kt["pv"] * 1e-3) / 1e9, 1)},
+        "append_us_per_layer": round(1000 * app_events[0][0].elapsed_time(app_events[0][1]) / (args.kernel_steps * n_lay), 2),
+        "hbm_read_ceiling": ceiling,
         "graph": bool(args.graph),
         "wall_s_timed": round(wall, 3),
         "roofline": {"kernel": dom_name, "launches_timed": args.kernel_steps * n_lay,

@@ -273,7 +273,20 @@ const char* kvq_status_string(int status);
 /* ABI version of this header (bumped on any incompatible change). */
 int kvq_abi_version(void);
 
-#define KVQ_ABI_VERSION 3
+/*
+ * Streaming-read probe (measurement only): reads every byte of a device buffer once with
+ * 16-byte loads, so that bytes / time is the HBM read bandwidth a plain kernel reaches on
+ * this device, the practical ceiling beside the quoted peak (the pages call decode memory-
+ * and bandwidth-bound: summary page, abstract paragraph).
+ *   buf    device buffer, 16-byte aligned; bytes a multiple of 16 (0 enqueues nothing).
+ *   sink   device uint32; receives 0x9e3779b9 when a thread's XOR of the 32-bit words it
+ *          read equals that value, and is untouched otherwise (the conditional store keeps
+ *          the loads from being optimised away).
+ * Errors: KVQ_ERR_INVALID for a misaligned buffer or size, or null pointers.
+ */
+int kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+#define KVQ_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

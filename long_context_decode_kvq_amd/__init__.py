@@ -23,10 +23,10 @@ STATUS_NAMES = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID", -2: "KVQ_ERR_UNSUPPORTED",
                 -3: "KVQ_ERR_CAPACITY", -4: "KVQ_ERR_WORKSPACE", -5: "KVQ_ERR_HIP"}
 EXPORTED = ("kvq_cache_sizes", "kvq_workspace_bytes", "kvq_quantize_append", "kvq_qk_matvec",
             "kvq_pv_matvec", "kvq_decode_attention", "kvq_key_scale", "kvq_key_threshold_workspace_bytes",
-            "kvq_key_threshold", "kvq_fit_workspace_bytes", "kvq_fit_codebook",
+            "kvq_key_threshold", "kvq_fit_workspace_bytes", "kvq_fit_codebook", "kvq_stream_read",
             "kvq_fp16_qk_matvec", "kvq_fp16_pv_matvec", "kvq_status_string",
             "kvq_abi_version")
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class KvqError(RuntimeError):
@@ -97,6 +97,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_fp16_qk_matvec.restype = ctypes.c_int
     lib.kvq_fp16_pv_matvec.argtypes = [ctypes.POINTER(Shape), P, P, P, P, P, SZ, I32, P]
     lib.kvq_fp16_pv_matvec.restype = ctypes.c_int
+    lib.kvq_stream_read.argtypes = [P, SZ, P, P]
+    lib.kvq_stream_read.restype = ctypes.c_int
     lib.kvq_status_string.argtypes = [ctypes.c_int]
     lib.kvq_status_string.restype = ctypes.c_char_p
     lib.kvq_abi_version.argtypes = []
@@ -414,3 +416,11 @@ def key_threshold(cfg: CacheConfig, keys: torch.Tensor, outlier_frac: float, out
                                           _stream(stream))
     _check("kvq_key_threshold", st)
     return out
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """kvq_stream_read: read every byte of a contiguous device tensor once (measurement)."""
+    assert buf.is_contiguous() and sink.dtype == torch.int32 and sink.numel() >= 1
+    nbytes = buf.numel() * buf.element_size()
+    _check("kvq_stream_read", load_library().kvq_stream_read(buf.data_ptr() if nbytes else None, nbytes,
+                                                             sink.data_ptr(), _stream(stream)))

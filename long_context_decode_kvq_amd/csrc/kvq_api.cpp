@@ -297,6 +297,14 @@ int kvq_key_threshold(const kvq_shape* s, const uint16_t* keys, int32_t n_tokens
                                               workspace, stream));
 }
 
+// ---- measurement ----------------------------------------------------------------------
+
+int kvq_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes % 16 != 0 || (bytes > 0 && (!buf || !sink))) return KVQ_ERR_INVALID;
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return KVQ_ERR_INVALID;
+  return hip_status(kvq::launch_stream_read(buf, bytes, sink, stream));
+}
+
 // ---- codebook fitting ---------------------------------------------------------------
 
 size_t kvq_fit_workspace_bytes(void) { return kvq::fit_workspace_bytes(); }

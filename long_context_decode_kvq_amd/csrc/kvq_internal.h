@@ -112,5 +112,7 @@ size_t fit_workspace_bytes();
 hipError_t launch_fit_codebook(int bits, const float* u, long long n, int iters, uint16_t* out, void* workspace,
                                hipStream_t s);
 hipError_t launch_fp16_pv(int group, int batch, const Fp16Args& a, hipStream_t s);
+// Streaming-read probe: reads bytes / 16 16-byte words of buf once.
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace kvq

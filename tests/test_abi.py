@@ -174,3 +174,11 @@ def test_key_threshold_entry_point_rejects_before_launch():
     assert T(ctypes.byref(shape), p, 10, 0.01, p, None, ws, None) == -4          # no workspace
     assert T(ctypes.byref(shape), p, 10, 0.01, p, p, ws - 1, None) == -4         # short workspace
     assert T(ctypes.byref(cfg(head_dim=64).shape()), p, 10, 0.01, p, p, ws, None) == -2
+
+
+def test_stream_read_rejects_before_launch():
+    lib = kvq.load_library()
+    assert lib.kvq_stream_read(4096, 100, 4096, None) == -1      # size not a multiple of 16
+    assert lib.kvq_stream_read(4104, 160, 4096, None) == -1      # misaligned buffer
+    assert lib.kvq_stream_read(None, 160, 4096, None) == -1      # no buffer
+    assert lib.kvq_stream_read(4096, 160, None, None) == -1      # no sink
