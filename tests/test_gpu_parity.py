@@ -170,15 +170,17 @@ def test_decode_is_deterministic(built):
             assert np.all(np.abs(o1[b, hq] - o2[b, hq]) <= n_terms * 2.0 ** -24 * scale + 1e-30)
 
 
-def test_device_position_appends_match_oracle():
+@pytest.mark.parametrize("key_outliers", [0, 1])
+def test_device_position_appends_match_oracle(key_outliers):
     """Appends that read their positions from the device seq_len (no host lengths) give
     the same cache as host-positioned appends, advance seq_len, and drop tokens of a
-    sequence without room while leaving its length unchanged."""
+    sequence without room while leaving its length unchanged (both key outlier rules)."""
     import long_context_decode_kvq_amd as kvq
     from kvq_testlib import stack_new
     wl = _wl("llama3_8b_gqa_b16_64k", batch=3, n_q_heads=4, n_kv_heads=2, seq_len=200)
     lens = np.array([190, 127, 62])
-    case = Case(wl, seed=5, lens=lens, device="cuda", max_seq=192)
+    ks = synth.key_scale(5, wl, quantile=0.99) if key_outliers else None
+    case = Case(wl, seed=5, lens=lens, device="cuda", max_seq=192, k_scale=ks, key_outliers=key_outliers)
     cache = case.build_gpu(upto=np.minimum(lens, 60))  # host positions for the first 60 tokens
     pos = np.minimum(lens, 60)
     while (pos < lens).any():
@@ -206,16 +208,19 @@ def test_device_position_appends_match_oracle():
     assert torch.equal(before, cache.k_codes)
 
 
-def test_graph_replay_of_decode_step_matches_eager():
+@pytest.mark.parametrize("key_outliers", [0, 1])
+def test_graph_replay_of_decode_step_matches_eager(key_outliers):
     """A decode step (device-positioned append, q.K^T, softmax.V) recorded once in a HIP
     graph and replayed several times, with eager work in between, gives every step the
-    same result as running the same step eagerly on an identical cache."""
+    same result as running the same step eagerly on an identical cache (both key outlier
+    rules)."""
     import long_context_decode_kvq_amd as kvq
     from kvq_testlib import stack_new
     wl = _wl("llama7b_32k", n_q_heads=4, n_kv_heads=4, seq_len=600)
     lens = np.array([600])
     steps = 4
-    case = Case(wl, seed=7, lens=lens + steps, device="cuda")
+    ks = synth.key_scale(7, wl, quantile=0.99) if key_outliers else None
+    case = Case(wl, seed=7, lens=lens + steps, device="cuda", k_scale=ks, key_outliers=key_outliers)
     pre = [int(lens[0])]
     c_eager = Case.__new__(Case)
     c_eager.__dict__.update(case.__dict__)
@@ -250,6 +255,9 @@ def test_graph_replay_of_decode_step_matches_eager():
         o_g, o_e = bufs_g.out.cpu().numpy(), bufs_e.out.cpu().numpy()
         assert np.allclose(o_g, o_e, rtol=1e-5, atol=1e-6)
     assert torch.equal(cache_g.k_codes, cache_e.k_codes) and torch.equal(cache_g.v_codes, cache_e.v_codes)
+    for kind in ("k", "v"):
+        for a, b in zip(cache_g.outliers(kind), cache_e.outliers(kind)):
+            assert torch.equal(a, b)
 
 
 # name -> (workload, lens): several split parts per stream for every group size, plus an
