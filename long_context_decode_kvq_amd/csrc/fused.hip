@@ -211,13 +211,16 @@ __global__ __launch_bounds__(kFuseThreads) void fused_decode_kernel(QkArgs a, Pv
     if (lane < 8) pab[b * kHalf + P] = make_float2(pa_, pb_);
     static_assert(KB == 2 || KB == 3, "2- and 3-bit keys");
     if constexpr (KB == 3) {
-      // wave w fills the rows of pairs w + 8 m, m < 8; lane m holds their coefficients
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int i = wave + kFuseWaves * m;
-        const float al = lane_f32(c1.x, m), be = lane_f32(c1.y, m), ga = lane_f32(c1.z, m), nd = lane_f32(c1.w, m);
-        T[i * kNe + lane] = make_float2(fmaf(al, cba, ga * cbb), fmaf(be, cba, nd * cbb));
-      }
+      // wave w fills the rows of pairs w + 8 m, m < 8; lane m of every 16-lane row holds
+      // their coefficients (lane l prepares pair w + 8 (l & 7)) and hands them over by DPP
+      // row broadcast inside the multiplies
+      float4 cc = c1;
+      // at least two wait states between these VALU writes and their DPP reads
+      asm volatile("s_nop 1" : "+v"(cc.x), "+v"(cc.y), "+v"(cc.z), "+v"(cc.w));
+      static_for<0, 8>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        T[(wave + kFuseWaves * m) * kNe + lane] = lut_entry_bcast<m>(cc.x, cc.y, cc.z, cc.w, cba, cbb);
+      });
     } else {
       // 16 entries per row: one fill step covers the rows of 4 pairs, m = 4 f + (lane >> 4)
 #pragma unroll

@@ -29,6 +29,22 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// One 3-bit table entry (A, B) = (al cba + ga cbb, be cba + nd cbb) whose four
+// coefficients come from lane N of the lane's 16-lane row, by DPP row broadcasts inside
+// the multiplies (no separate lane reads).  The DPP sources must have been written at
+// least two wait states earlier.
+template <int N>
+__device__ __forceinline__ float2 lut_entry_bcast(float al, float be, float ga, float nd, float cba, float cbb) {
+  float A, B;
+  asm("v_mul_f32_dpp %0, %4, %6 row_newbcast:%8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %1, %5, %6 row_newbcast:%8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %0, %2, %7 row_newbcast:%8 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_fmac_f32_dpp %1, %3, %7 row_newbcast:%8 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "=&v"(A), "=&v"(B)
+      : "v"(al), "v"(be), "v"(ga), "v"(nd), "v"(cbb), "v"(cba), "i"(N));
+  return make_float2(A, B);
+}
+
 // Wave reductions: four DPP steps combine the 16 lanes of each row (xor 1, xor 2, half-row
 // mirror, row mirror), then the four row results are read into scalar registers.  Every
 // lane gets the result; no LDS round trips.
