@@ -11,7 +11,7 @@
 //   * R(-t0), folded into the query once per tile (lane i handles rotary pair i; the
 //     tile-base phase is formed once per wave from a float64 angle and then advanced by
 //     the fixed step 64 * theta_i), and
-//   * R(tau), tau = lane < 64, from a per-block table (the first KVQ_QK_REG_PAIRS pairs
+//   * R(tau), tau = lane < 64, from a per-block table (the first kRegPairs pairs
 //     copied into registers, the rest read from LDS).
 // The record keeps the two halves of rotary pair i side by side, so one 2b-bit field
 // indexes a small shared table of fp16 pairs (cb[a], cb[b]); the fp16 values feed
@@ -21,8 +21,11 @@
 //   l += cb[a] * (s_i q'_i E_r + s_i q'_{i+64} E_i) + cb[b] * (s_{i+64} q'_{i+64} E_r - s_{i+64} q'_i E_i)
 // (8 VALU ops per token and pair); the four coefficients reach the lanes through DPP row
 // broadcasts inside the multiplies, so the pair loop reads LDS only for the table lookup
-// (and R(tau) when it is not in registers).  With g > 1 query heads the key is dequantized and rotated once and
-// dotted with every head (8 + 2g ops).
+// (and R(tau) when it is not in registers).  With g > 1 query heads the key is dequantized
+// and rotated once and dotted with every head: with 2/3-bit keys the dequantized pair
+// (cb[a] s_i, cb[b] s_{i+64}) comes from a per-block table of 64 rows (one per rotary
+// pair, built once), so a key and pair cost the field address, one 8-byte table read, the
+// rotation (4 ops) and 2g FMAs; 4-bit keys read the fp16 codebook pair and scale it.
 #include <algorithm>
 #include <type_traits>
 
@@ -68,8 +71,8 @@ struct Rec {
   uint32_t oi[2], ov[2];  // its first two outliers: channels and fp16 value bits
 };
 constexpr int kPartials = 4;  // partial sums per logit
-constexpr int kRegPairs = KVQ_QK_REG_PAIRS;
-static_assert(kRegPairs >= 0 && kRegPairs <= kHalf, "register pairs out of range");
+constexpr int kRegPairsDefault = KVQ_QK_REG_PAIRS;
+static_assert(kRegPairsDefault >= 0 && kRegPairsDefault <= kHalf, "register pairs out of range");
 
 template <int KB, int G>
 __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
@@ -77,10 +80,18 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   constexpr int kRecWords = 4 * KB;
   constexpr int kPairEntries = 1 << (2 * KB);
   constexpr bool kFoldScale = G == 1;
+  // With several query heads and 2/3-bit keys, each rotary pair has its own table of the
+  // scaled codebook pair (cb[a] s_i, cb[b] s_{i+64}) (64 rows of 2^(2b) float pairs, built
+  // once per block): one 8-byte read per key and pair, no conversion or scaling.
+  constexpr bool kPairTab = !kFoldScale && KB <= 3;
+  // R(tau) of the first kRegPairs pairs is held in registers (where the pair table left
+  // room: 2 and 4 heads), the rest read from LDS
+  constexpr int kRegPairs = kPairTab && G <= 4 ? 32 : kRegPairsDefault;
 
   __shared__ float2 et[kHalf][kTile];       // R(tau) for pair i: (cos, sin) of tau * theta_i
   using Tab = RepTable<kPairEntries>;
-  __shared__ uint32_t lutp[Tab::kWords];    // fp16 (cb[a], cb[b]) for a pair field a | b << KB, replicated
+  __shared__ uint32_t lutp[kPairTab ? 1 : Tab::kWords];  // fp16 (cb[a], cb[b]) for a pair field a | b << KB, replicated
+  __shared__ float2 ptab[kPairTab ? kHalf : 1][kPairTab ? kPairEntries : 1];  // (cb[a] s_i, cb[b] s_{i+64})
   __shared__ float ks[kHeadDim];
   __shared__ float2 ksp[kHalf];             // (s_i, s_{i+64})
   __shared__ float2 qr[kWaves][G][kHalf];   // per-wave tile-rotated query pairs
@@ -190,7 +201,7 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   // ---- per-block tables -----------------------------------------------------------
   ks[tid & (kHeadDim - 1)] = ks_own;
   ksp[tid & (kHalf - 1)] = make_float2(ks_lo, ks_hi);
-  for (int wd = tid; wd < Tab::kWords; wd += 256) {  // word wd holds entry wd / copies
+  for (int wd = tid; wd < (kPairTab ? 0 : Tab::kWords); wd += 256) {  // word wd holds entry wd / copies
     const int e = wd / Tab::kCopies;                 // codebook entries from the lanes holding them
     const uint32_t lo = static_cast<uint32_t>(__shfl(static_cast<int>(cb_lo), e & (kNc - 1))) & 0xffffu;
     const uint32_t hi = static_cast<uint32_t>(__shfl(static_cast<int>(cb_lo), e >> KB)) & 0xffffu;
@@ -230,7 +241,21 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   }
   // value every outlier slot decodes to: the codebook entry nearest zero
   const float zc = zero_code_value<kNc>(cb_lo, lane);
+  // this thread's entry of every pair table row it fills: the entry index is the same for
+  // all of them (256 threads, a multiple of the row length)
+  const int pt_ent = tid & (kPairEntries - 1);
+  const float pt_cba = half_bits_to_float(static_cast<uint32_t>(__shfl(static_cast<int>(cb_lo), pt_ent & (kNc - 1))) & 0xffffu);
+  const float pt_cbb = half_bits_to_float(static_cast<uint32_t>(__shfl(static_cast<int>(cb_lo), pt_ent >> KB)) & 0xffffu);
   block_lds_barrier();
+  if constexpr (kPairTab) {  // ksp is in LDS now
+    constexpr int kRowsPerPass = 256 / kPairEntries;
+#pragma unroll
+    for (int r = tid / kPairEntries; r < kHalf; r += kRowsPerPass) {
+      const float2 sp = ksp[r];
+      ptab[r][pt_ent] = make_float2(pt_cba * sp.x, pt_cbb * sp.y);
+    }
+    block_lds_barrier();
+  }
   float s_lo[kSlots], s_hi[kSlots];  // scales of the slot pairs
   float bc[kSlots], bs[kSlots], sc[kSlots], ss[kSlots];  // their tile-base phase and per-tile step
 #pragma unroll
@@ -257,6 +282,8 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
 
   const int my_slot = lane >> 4;
   const uint32_t tab_base = Tab::lane_base(lane);
+  const uint32_t pt_base = lds_address(&ptab[0][0]);
+  const unsigned char* lds0 = reinterpret_cast<const unsigned char*>(&ptab[0][0]) - pt_base;  // LDS address -> pointer
   static_assert(kSlots == 4, "four 16-lane rows");
   auto pick = [&](float v0, float v1, float v2, float v3) {
     return my_slot == 0 ? v0 : my_slot == 1 ? v1 : my_slot == 2 ? v2 : v3;
@@ -310,8 +337,10 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
 
     static_for<0, kHalf>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      const uint32_t e2 = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(lutp) +
-                                                            Tab::at(field<2 * KB, 2 * KB * i>(d.w), tab_base));
+      uint32_t e2 = 0;  // the replicated fp16 table's entry (the paths without the pair table)
+      if constexpr (!kPairTab)
+        e2 = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(lutp) +
+                                                Tab::at(field<2 * KB, 2 * KB * i>(d.w), tab_base));
       float cr, ci;
       if constexpr (i < kRegPairs) {
         cr = er[i];
@@ -325,11 +354,19 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
         accp[0][i % kPartials] =
             pair_term<i % 16>(accp[0][i % kPartials], e2, cr, ci, alp[i / 16], bet[i / 16], gam[i / 16], ndl[i / 16]);
       } else {
-        const float cb_a = half_bits_to_float(e2 & 0xffffu);
-        const float cb_b = half_bits_to_float(e2 >> 16);
-        const float2 sp = ksp[i];
-        const float xa = cb_a * sp.x;
-        const float xb = cb_b * sp.y;
+        float xa, xb;
+        if constexpr (kPairTab) {
+          const float2 x = *reinterpret_cast<const float2*>(
+              lds0 + field_addr<2 * KB, 2 * KB * i, 3>(d.w, pt_base) + i * kPairEntries * 8);
+          xa = x.x;
+          xb = x.y;
+        } else {
+          const float cb_a = half_bits_to_float(e2 & 0xffffu);
+          const float cb_b = half_bits_to_float(e2 >> 16);
+          const float2 sp = ksp[i];
+          xa = cb_a * sp.x;
+          xb = cb_b * sp.y;
+        }
         const float ya = xa * cr - xb * ci;
         const float yb = xa * ci + xb * cr;
 #pragma unroll

@@ -50,6 +50,11 @@ CASES = {
     "mha2_2bit_k3": (_wl("llama7b_1m_2bit", n_q_heads=2, n_kv_heads=2, seq_len=1100, outlier_frac=0.02), [1100], None),
     "gqa4_k5_ragged": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=4, n_kv_heads=1, seq_len=900, outlier_frac=0.035),
                        [900, 333], None),
+    # grouped heads with 2-bit keys (the per-pair table path of the general kernel)
+    "gqa2_2bit": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=4, n_kv_heads=2, seq_len=800, k_bits=2),
+                  [800, 391], None),
+    "gqa8_2bit": (_wl("llama3_8b_gqa_b16_64k", batch=1, n_q_heads=8, n_kv_heads=1, seq_len=1000, k_bits=2, v_bits=2),
+                  [1000], None),
     # the per-channel key outlier rule (key_outliers = 1): the frozen key scale is a
     # per-channel quantile of |key| over the calibration draw and doubles as the threshold
     "pc_mha4_3bit_k2": (_wl("llama7b_32k", n_q_heads=4, n_kv_heads=4, seq_len=1100), [1100], None),
