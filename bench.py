@@ -534,6 +534,9 @@ def main():
     qk_b, pv_b, app_b = algorithmic_bytes(wl, L_mean)
     step_bytes = args.layers * (qk_b + pv_b + app_b)
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    # the same without the logits (written by q.K^T, read by softmax.V: 8 bytes per query
+    # head and token), the KV-only figure a single-pass kernel would be judged by
+    kv_only_gbs = (step_bytes - args.layers * 8 * wl.batch * wl.n_q_heads * L_mean) / (ms_step * 1e-3) / 1e9
     kv_tok_s = args.layers * wl.batch * L_mean / (ms_step * 1e-3)
 
     n_lay = len(layers)
@@ -565,6 +568,7 @@ def main():
                    "seq_len": wl.seq_len, "k_bits": wl.k_bits, "v_bits": wl.v_bits,
                    "outliers_per_vector": wl.n_outliers, "new_tokens_per_step": wl.n_new},
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "kv_only_gbs": round(kv_only_gbs, 1),
         "kv_tokens_per_s": round(kv_tok_s, 1),
         "kernel_ms": {k: round(v, 5) for k, v in kt.items()},
         "kernel_gbs": {"qk": round(qk_bk / (kt["qk"] * 1e-3) / 1e9, 1),
