@@ -140,9 +140,12 @@ __global__ __launch_bounds__(kFuseThreads) void fused_decode_kernel(QkArgs a, Pv
   };
 
   // ---- set-up inputs, then the first super-tile's data --------------------------------
-  // Lane l of wave w prepares the table coefficients of pair P = w + 8 (l & 7); lanes
-  // 0..7 of the wave hold the eight pairs whose rows the wave fills.
-  const int P = wave + kFuseWaves * (lane & 7);
+  // Lane l of wave w prepares the table coefficients of one of the eight pairs w + 8 m
+  // whose rows the wave fills, placed for the DPP row broadcasts of the build: 3-bit rows,
+  // m = l & 7 (lane m of every 16-lane row holds pair w + 8 m); 2-bit rows, lane 16 r + f
+  // prepares m = 4 f + r (fill step f finds its row's pair at lane f of the row).
+  const int P = KB == 3 ? wave + kFuseWaves * (lane & 7) : wave + kFuseWaves * ((lane >> 4) + 4 * (lane & 1));
+  const bool writes_pab = KB == 3 ? lane < 8 : (lane & 14) == 0;  // one lane per pair
   const size_t qbase = (static_cast<size_t>(seq) * a.n_q_heads + kvh) * kHeadDim;
   uint32_t qraw[2];
   if (a.q_is_fp16) {  // wave-uniform; both paths issue the same loads
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(kFuseThreads) void fused_decode_kernel(QkArgs a, Pv
     const float pa_ = qv[0] * cs + qv[1] * sn;  // R(-t0 theta) q
     const float pb_ = qv[1] * cs - qv[0] * sn;
     const float4 c1 = make_float4(sP_lo * pa_, sP_lo * pb_, sP_hi * pb_, -(sP_hi * pa_));  // alpha, beta, gamma, -delta
-    if (lane < 8) pab[b * kHalf + P] = make_float2(pa_, pb_);
+    if (writes_pab) pab[b * kHalf + P] = make_float2(pa_, pb_);
     static_assert(KB == 2 || KB == 3, "2- and 3-bit keys");
     if constexpr (KB == 3) {
       // wave w fills the rows of pairs w + 8 m, m < 8; lane m of every 16-lane row holds
@@ -222,14 +225,16 @@ __global__ __launch_bounds__(kFuseThreads) void fused_decode_kernel(QkArgs a, Pv
         T[(wave + kFuseWaves * m) * kNe + lane] = lut_entry_bcast<m>(cc.x, cc.y, cc.z, cc.w, cba, cbb);
       });
     } else {
-      // 16 entries per row: one fill step covers the rows of 4 pairs, m = 4 f + (lane >> 4)
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int m = 4 * f + (lane >> 4);
-        const float4 cc = make_float4(__shfl(c1.x, m), __shfl(c1.y, m), __shfl(c1.z, m), __shfl(c1.w, m));
-        const int i = wave + kFuseWaves * m;
-        T[i * kNe + (lane & 15)] = make_float2(fmaf(cc.x, cba, cc.z * cbb), fmaf(cc.y, cba, cc.w * cbb));
-      }
+      // 16 entries per row: fill step f covers the rows of 4 pairs, m = 4 f + (lane >> 4),
+      // whose coefficients lane f of each 16-lane row holds (DPP row broadcast)
+      float4 cc = c1;
+      // at least two wait states between these VALU writes and their DPP reads
+      asm volatile("s_nop 1" : "+v"(cc.x), "+v"(cc.y), "+v"(cc.z), "+v"(cc.w));
+      static_for<0, 2>([&](auto fc) {
+        constexpr int f = decltype(fc)::value;
+        const int i = wave + kFuseWaves * (4 * f + (lane >> 4));
+        T[i * kNe + (lane & 15)] = lut_entry_bcast<f>(cc.x, cc.y, cc.z, cc.w, cba, cbb);
+      });
     }
   };
 
