@@ -62,20 +62,31 @@ __device__ __forceinline__ uint32_t lane_u32(uint32_t v, int l) {
 __device__ __forceinline__ float lane_f32(float v, int l) {
   return __builtin_bit_cast(float, lane_u32(__builtin_bit_cast(uint32_t, v), l));
 }
+// Wave maxima: each step is one max in DPP form (the four row steps above, then lane 15 of
+// each row into the next row and lane 31 into the upper half), so lane 63 ends with the
+// maximum, read into a scalar register: seven VALU instructions, where max over separately
+// moved DPP values costs two or three per step (the float form also re-canonicalises).
+// Each DPP read follows the write of its source by two wait states (s_nop 1).  The float
+// form is for finite or infinite inputs (no NaN), as a maximum of logits, weights or
+// magnitudes is.
+#define KVQ_WAVE_MAX_STEPS(OP)                                                       \
+  "s_nop 1\n\t" OP "_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t" \
+  "s_nop 1\n\t" OP "_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t" \
+  "s_nop 1\n\t" OP "_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf\n\t"      \
+  "s_nop 1\n\t" OP "_dpp %0, %0, %0 row_mirror row_mask:0xf bank_mask:0xf\n\t"           \
+  "s_nop 1\n\t" OP "_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"         \
+  "s_nop 1\n\t" OP "_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf"
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u32<0xB1>(v));
-  v = max(v, dpp_u32<0x4E>(v));
-  v = max(v, dpp_u32<0x141>(v));
-  v = max(v, dpp_u32<0x140>(v));
-  return max(max(lane_u32(v, 0), lane_u32(v, 16)), max(lane_u32(v, 32), lane_u32(v, 48)));
+  uint32_t r;
+  asm(KVQ_WAVE_MAX_STEPS("v_max_u32") : "=&v"(r) : "v"(v));
+  return lane_u32(r, 63);
 }
 __device__ __forceinline__ float wave_max_f32(float v) {
-  v = fmaxf(v, dpp_f32<0xB1>(v));
-  v = fmaxf(v, dpp_f32<0x4E>(v));
-  v = fmaxf(v, dpp_f32<0x141>(v));
-  v = fmaxf(v, dpp_f32<0x140>(v));
-  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
+  float r;
+  asm(KVQ_WAVE_MAX_STEPS("v_max_f32") : "=&v"(r) : "v"(v));
+  return lane_f32(r, 63);
 }
+#undef KVQ_WAVE_MAX_STEPS
 __device__ __forceinline__ float wave_sum_f32(float v) {
   v += dpp_f32<0xB1>(v);
   v += dpp_f32<0x4E>(v);
