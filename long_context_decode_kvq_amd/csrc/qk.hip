@@ -77,7 +77,6 @@ static_assert(kRegPairsDefault >= 0 && kRegPairsDefault <= kHalf, "register pair
 template <int KB, int G>
 __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   constexpr int kNc = 1 << KB;
-  constexpr int kRecWords = 4 * KB;
   constexpr int kPairEntries = 1 << (2 * KB);
   constexpr bool kFoldScale = G == 1;
   // With several query heads and 2/3-bit keys, each rotary pair has its own table of the
@@ -249,7 +248,6 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   block_lds_barrier();
   if constexpr (kPairTab) {  // ksp is in LDS now
     constexpr int kRowsPerPass = 256 / kPairEntries;
-#pragma unroll
     for (int r = tid / kPairEntries; r < kHalf; r += kRowsPerPass) {
       const float2 sp = ksp[r];
       ptab[r][pt_ent] = make_float2(pt_cba * sp.x, pt_cbb * sp.y);

@@ -52,7 +52,6 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   using Sh = LutShape<KB>;
   constexpr int kNc = Sh::kNc;
   constexpr int kNe = Sh::kNe;
-  constexpr int kRecWords = 4 * KB;
 
   extern __shared__ __align__(16) unsigned char lds[];
   float2* lut = reinterpret_cast<float2*>(lds);                            // [bufs][64][kNe] (A, B)
