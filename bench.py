@@ -382,7 +382,7 @@ def main():
         summarize_counters(*args.summarize_counters, args.workload)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "kvq runs on one GPU; --gpus must be 1 "
                           "(sharding across GPUs is designed, not built)"}))
         sys.exit(2)
     import torch
