@@ -604,7 +604,7 @@ def main():
     if not args.no_cpu_baseline:
         n_streams = min(args.cpu_heads, wl.batch * wl.n_kv_heads)
         line["cpu_baseline"] = cpu_baseline(wl, args.seed * 1000, n_streams, args.cpu_layers)
-        # the machine's CPU share is 16 threads per GPU, whatever the host reports
+        # at most 16 worker processes (a host's share per GPU), whatever the host reports
         workers = max(1, min(16, len(os.sched_getaffinity(0))))
         if workers > 1:
             line["cpu_baseline_parallel"] = cpu_baseline_parallel(wl, args.seed * 1000, n_streams, args.cpu_layers,
