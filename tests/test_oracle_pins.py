@@ -115,6 +115,95 @@ def test_key_scale_axis_is_the_channel():
     assert np.array_equal(c1, c2)
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_uniform_codebook_keys_are_the_textbook_per_channel_quantizer(bits):
+    """Uniform codebook, k = 0, a different non-unit scale on every channel: key
+    quantization is the textbook per-channel symmetric quantizer
+    code_c = round((x_c / s_c + 1)(2^b - 1)/2) (clamped to the grid), it decodes to
+    s_c (-1 + 2 code_c / (2^b - 1)), and each dense entry is within half a step,
+    s_c / (2^b - 1), of x_c.  A decode that drops, swaps or transposes the per-channel
+    scale misses all three."""
+    rng = np.random.default_rng(70 + bits)
+    s = (0.5 + np.arange(D) * 0.0625).astype(np.float32)   # 0.5 .. 8.4375, all distinct
+    x = (rng.uniform(-1, 1, size=(96, D)) * s[None, :]).astype(np.float16)
+    cb = synth.uniform_codebook(bits)
+    codes, idx, val = oracle.quantize_keys(x, s, cb, 0)
+    assert idx.shape == (96, 0) and val.shape == (96, 0)
+    levels = (1 << bits) - 1
+    t = (x.astype(np.float64) / s.astype(np.float64)[None, :] + 1.0) * levels / 2.0
+    expect = np.clip(np.floor(t + 0.5), 0, levels)
+    near_tie = np.abs(t - np.floor(t) - 0.5) < 1e-5
+    assert np.array_equal(codes[~near_tie], expect[~near_tie].astype(np.uint8))
+    deq = oracle.dequant_keys(codes, idx, val, s, cb)
+    textbook = s.astype(np.float64)[None, :] * (-1.0 + 2.0 * codes.astype(np.float64) / levels)
+    assert np.allclose(deq, textbook, rtol=1e-6, atol=0)
+    err = np.abs(deq - x.astype(np.float64))
+    assert np.all(err <= s.astype(np.float64)[None, :] / levels * (1 + 1e-6))
+
+
+def _hand_example():
+    """A two-token stream whose logits, outputs and tolerance scales are derived by hand.
+
+    Key and value codebook cb = (-1, -1/2, 1/2, 1) (2-bit), k = 0.  Key scales s_0 = 2,
+    s_64 = 4, every other channel 1.  Both key vectors hold x_0 = 1, x_64 = -4 and zeros
+    elsewhere: u_0 = 1/2 -> code 2 (1/2), u_64 = -1 -> code 0 (-1), so the dequantized
+    key has k~_0 = 1/2 * 2 = 1 and k~_64 = -1 * 4 = -4 (a zero entry, u = 0, ties between
+    -1/2 and 1/2 and takes -1/2; the query is zero on those channels).  The query is
+    q_0 = 1, q_64 = 2, zero elsewhere.  Rotary pair (0, 64) turns by t radians (theta_0 = 1),
+    so y_0 = cos t + 4 sin t, y_64 = sin t - 4 cos t and
+        l_t = sm (q_0 y_0 + q_64 y_64) = sm (6 sin t - 7 cos t),
+        tolerance scale_t = sm (|y_0| + 2 |y_64|).
+    Values: token 0 holds v_0 = 2, v_1 = -1 (max |v| = 2: codes 3 and 1, decoded 2 and
+    -1), token 1 holds v_0 = -4, v_1 = 4 (scale 4: codes 0 and 3); every other channel is
+    zero and decodes to the zero code -1/2 times the token's scale: -1 and -2."""
+    cb = np.float32([-1.0, -0.5, 0.5, 1.0])
+    s = np.ones(D, np.float32)
+    s[0], s[64] = 2.0, 4.0
+    k16 = np.zeros((2, D), np.float16)
+    k16[:, 0], k16[:, 64] = 1.0, -4.0
+    v16 = np.zeros((2, D), np.float16)
+    v16[0, :2] = [2.0, -1.0]
+    v16[1, :2] = [-4.0, 4.0]
+    q = np.zeros(D)
+    q[0], q[64] = 1.0, 2.0
+    sm = 1.0 / math.sqrt(D)
+    logits = np.array([sm * (6 * math.sin(t) - 7 * math.cos(t)) for t in (0, 1)])
+    tol_l = np.array([sm * (abs(math.cos(t) + 4 * math.sin(t)) + 2 * abs(math.sin(t) - 4 * math.cos(t)))
+                      for t in (0, 1)])
+    p1 = 1.0 / (1.0 + math.exp(logits[0] - logits[1]))
+    p = np.array([1.0 - p1, p1])
+    v_dec = np.full((2, D), 0.0)
+    v_dec[0], v_dec[1] = -1.0, -2.0
+    v_dec[0, :2] = [2.0, -1.0]
+    v_dec[1, :2] = [-4.0, 4.0]
+    out = p @ v_dec
+    tol_o = p @ np.abs(v_dec)
+    return dict(cb=cb, s=s, k16=k16, v16=v16, q=q, sm=sm, logits=logits, tol_l=tol_l, out=out, tol_o=tol_o)
+
+
+def test_per_channel_key_decode_hand_example():
+    """decode_head on the dense path with channel-dependent key scales, against the
+    hand-derived logits and output of _hand_example."""
+    e = _hand_example()
+    c = oracle.quantize_stream(e["k16"], e["v16"], e["s"], e["cb"], e["cb"], 0)
+    assert list(c.k_codes[0, [0, 64, 1]]) == [2, 0, 1]
+    logits, out = oracle.decode_head(e["q"], c, e["s"], e["cb"], e["cb"], 10000.0, e["sm"])
+    assert np.allclose(logits, e["logits"], rtol=0, atol=1e-12)
+    assert np.allclose(out, e["out"], rtol=0, atol=1e-12)
+
+
+def test_tolerance_scales_hand_example():
+    """The logit tolerance scale is sm * sum_c |q_c y_c| and the output one
+    sum_t p_t |v~_t,c|, on the hand-derived example (a dropped sm_scale, a signed sum or
+    unnormalised weights fail it)."""
+    e = _hand_example()
+    c = oracle.quantize_stream(e["k16"], e["v16"], e["s"], e["cb"], e["cb"], 0)
+    tl = oracle.logit_tolerance_scale(e["q"], c, e["s"], e["cb"], 10000.0, e["sm"])
+    assert np.allclose(tl, e["tol_l"], rtol=0, atol=1e-12)
+    to = oracle.output_tolerance_scale(e["logits"], c, e["cb"])
+    assert np.allclose(to, e["tol_o"], rtol=0, atol=1e-12)
+
+
 def test_value_scale_is_per_vector_max_of_dense_part():
     rng = np.random.default_rng(12)
     cb = _fp16_codebook(rng, 3)
@@ -359,6 +448,37 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         test_key_threshold_special_cases()
     monkeypatch.setattr(oracle.kvquant, "exceed_budget", good_budget)
     monkeypatch.setattr(oracle, "exceed_budget", good_budget)
+
+    # 6. the per-channel key scale dropped from, or reversed across channels in, the decode
+    good_dk = oracle.kvquant.dequant_keys
+    for bad_scale in (lambda s: np.ones_like(np.asarray(s, np.float32)), lambda s: np.asarray(s)[::-1]):
+        def bad_dk(codes, out_idx, out_val, k_scale32, codebook32, f=bad_scale):
+            return good_dk(codes, out_idx, out_val, f(k_scale32), codebook32)
+        monkeypatch.setattr(oracle.kvquant, "dequant_keys", bad_dk)
+        monkeypatch.setattr(oracle, "dequant_keys", bad_dk)
+        with pytest.raises(AssertionError):
+            test_per_channel_key_decode_hand_example()
+        with pytest.raises(AssertionError):
+            test_uniform_codebook_keys_are_the_textbook_per_channel_quantizer(3)
+    monkeypatch.setattr(oracle.kvquant, "dequant_keys", good_dk)
+    monkeypatch.setattr(oracle, "dequant_keys", good_dk)
+
+    # 7. the logit tolerance without sm_scale; the output tolerance as a signed sum
+    good_tl, good_to = oracle.kvquant.logit_tolerance_scale, oracle.kvquant.output_tolerance_scale
+    monkeypatch.setattr(oracle, "logit_tolerance_scale",
+                        lambda q, c, ks, cb, base, sm, length=None: good_tl(q, c, ks, cb, base, 1.0, length))
+    with pytest.raises(AssertionError):
+        test_tolerance_scales_hand_example()
+    monkeypatch.setattr(oracle, "logit_tolerance_scale", good_tl)
+
+    def signed_to(logits, c, cb, length=None):
+        n = c.length if length is None else length
+        vd = oracle.dequant_values(c.v_codes[:n], c.v_idx[:n], c.v_val[:n], c.v_scale[:n], cb)
+        return np.abs(oracle.softmax(logits[:n]) @ vd)
+    monkeypatch.setattr(oracle, "output_tolerance_scale", signed_to)
+    with pytest.raises(AssertionError):
+        test_tolerance_scales_hand_example()
+    monkeypatch.setattr(oracle, "output_tolerance_scale", good_to)
 
 
 # ---- codebook fitting (unweighted k-means, oracle/codebook_fit.py) -----------------------
