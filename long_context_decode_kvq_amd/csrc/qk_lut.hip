@@ -7,17 +7,27 @@
 //
 // With a single query the rotated-query coefficients and the codebook fold into one
 // table per group of tiles.  For rotary pair i of a key at position t = T0 + tau (T0 the
-// first token of a super-tile of kWaves x 64 tokens, tau < 64 kWaves) with codes a (channel
-// i) and b (channel i + 64):
+// first token of a super-tile of kLutWaves x 64 tokens, tau < 64 kLutWaves) with codes a
+// (channel i) and b (channel i + 64):
 //   q . R(t) k = E_r(tau) A_i[a, b] + E_i(tau) B_i[a, b]
 //   A_i = s_i cb[a] p_a + s_{i+64} cb[b] p_b,  B_i = s_i cb[a] p_b - s_{i+64} cb[b] p_a
 // where (p_a, p_b) = R(-T0 theta_i) (q_i, q_{i+64}) and E(tau) = (cos, sin)(tau theta_i).
-// Lane = token: each lane keeps E(tau) of its own tau for all 64 pairs in registers, so a
-// pair costs one field extraction, one 8-byte table read and two FMAs.  The waves of a block
-// share the table of the super-tile: they build the next one (double-buffered) while
-// each computes its tile of the current one, with one block barrier per super-tile.
-// Outliers replace the zero code decoded at their channel: their correction uses the
-// hardware sine/cosine (argument in revolutions) at the outlier's pair.
+// Lane = token: each lane keeps E(tau) of its own tau for all 64 pairs in 128 registers,
+// so a pair costs one 8-byte table read, two FMAs and the table address.  The address is
+// the pair's code field times 8, formed by one shift and one mask (two single-rate
+// integer operations, where a bit-field extract and a shift-add are two FMA-rate ones);
+// the row of the pair and the table buffer are immediate offsets of the read (the main
+// loop is unrolled over the two buffers).
+//
+// The waves of a block share the table of a super-tile.  Between two block barriers
+// every wave computes its tile of super-tile s and fills its rows of the table of s + 1
+// (double-buffered), the coefficients reaching the lanes by DPP row broadcasts; one wave
+// (a different one each step) forms the rotated-query coefficients of all 64 pairs for
+// s + 2.  Operands that come from LDS (the build coefficients, each outlier's scale,
+// frequency and rotated-query pair) are requested before the pair loop and consumed after
+// it, so their latency hides behind the loop.  Outliers replace the zero code decoded at
+// their channel: their correction uses the hardware sine/cosine (argument in revolutions)
+// at the outlier's pair.
 #include <algorithm>
 #include <type_traits>
 
@@ -29,14 +39,21 @@ namespace {
 
 constexpr int kLutWaves = 8;                 // waves per block = tiles per super-tile
 constexpr int kLutThreads = 64 * kLutWaves;
+constexpr int kLutSuper = kLutWaves * kTile; // tokens per super-tile
 constexpr int kLutPrefetchOutliers = 2;      // outliers per token fetched with the record
+constexpr int kLutAhead = 7;                 // table reads in flight ahead of the FMAs (at most 15)
 
 template <int KB>
 struct LutShape {
   static constexpr int kNc = 1 << KB;
   static constexpr int kNe = kNc * kNc;               // code pairs (a | b << KB) per rotary pair
-  static constexpr int kBufs = 2;                     // double-buffered (2- and 3-bit codes only)
-  static constexpr int kBufBytes = kHalf * kNe * 8;   // 64 rows of (A, B) float pairs
+  static constexpr int kRowBytes = kNe * 8;           // (A, B) float pairs of one rotary pair
+  static constexpr int kBufBytes = kHalf * kRowBytes; // 64 rows
+  static constexpr uint32_t kMask = (kNe - 1) << 3;   // code field times 8
+  // tables, build coefficients, rotated-query pairs, key scales, frequencies (split and
+  // float64), query and scales per pair
+  static constexpr int kLdsBytes = 2 * kBufBytes + 2 * kHalf * 16 + 3 * kHalf * 8 + kHeadDim * 4 + kHalf * 8 +
+                                   kHalf * 16 + kHalf * 8;
 };
 
 template <int KB>
@@ -45,6 +62,33 @@ struct LutRec {
   uint32_t oi[2], ov[2];  // its first two outliers: channels and fp16 value bits
 };
 
+// Byte offset of pair I's (A, B) entry within its table row: its 2KB-bit code field
+// times 8, by a shift and a mask (single-rate VOP2 operations; a field that straddles two
+// words takes an align-bit first).
+template <int KB, int I, int N>
+__device__ __forceinline__ uint32_t entry_offset(const uint32_t (&w)[N]) {
+  constexpr int kBits = 2 * KB;
+  constexpr int pos = kBits * I;
+  constexpr int wi = pos / 32;
+  constexpr int sh = pos % 32;
+  constexpr uint32_t mask = LutShape<KB>::kMask;
+  static_assert(wi < N, "field outside the record");
+  uint32_t r;
+  if constexpr (sh + kBits <= 32) {
+    if constexpr (sh >= 3) {
+      asm("v_lshrrev_b32_e32 %0, %2, %1\n\tv_and_b32_e32 %0, %3, %0" : "=&v"(r) : "v"(w[wi]), "n"(sh - 3), "n"(mask));
+    } else {
+      asm("v_lshlrev_b32_e32 %0, %2, %1\n\tv_and_b32_e32 %0, %3, %0" : "=&v"(r) : "v"(w[wi]), "n"(3 - sh), "n"(mask));
+    }
+  } else {
+    static_assert(wi + 1 < N, "straddling field outside the record");
+    asm("v_alignbit_b32 %0, %1, %2, %3\n\tv_and_b32_e32 %0, %4, %0"
+        : "=&v"(r)
+        : "v"(w[wi + 1]), "v"(w[wi]), "n"(sh - 3), "n"(mask));
+  }
+  return r;
+}
+
 // kExtra: outliers beyond the first kLutPrefetchOutliers per token exist (read in a loop
 // of their own); without them that loop is compiled out.
 template <int KB, bool kExtra>
@@ -52,12 +96,18 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   using Sh = LutShape<KB>;
   constexpr int kNc = Sh::kNc;
   constexpr int kNe = Sh::kNe;
+  static_assert(KB == 2 || KB == 3, "2- and 3-bit keys");
 
-  extern __shared__ __align__(16) unsigned char lds[];
-  float2* lut = reinterpret_cast<float2*>(lds);                            // [bufs][64][kNe] (A, B)
-  float* ks = reinterpret_cast<float*>(lds + Sh::kBufs * Sh::kBufBytes);   // [128] key scales
-  float2* pab = reinterpret_cast<float2*>(ks + kHeadDim);                  // [bufs][64] (p_a, p_b)
-  float2* thl = pab + Sh::kBufs * kHalf;                                   // [64] theta_i/2pi split hi, lo
+  // statically sized, so that table offsets are compile-time LDS addresses (immediate
+  // offsets of the reads)
+  __shared__ __align__(16) unsigned char lds[Sh::kLdsBytes];
+  float2* lut = reinterpret_cast<float2*>(lds);                           // [2][64][kNe] (A, B)
+  float4* coef = reinterpret_cast<float4*>(lds + 2 * Sh::kBufBytes);      // [2][64] (alpha, beta, gamma, -delta)
+  float2* cpab = reinterpret_cast<float2*>(coef + 2 * kHalf);             // [3][64] (p_a, p_b)
+  float* ks = reinterpret_cast<float*>(cpab + 3 * kHalf);                 // [128] key scales
+  float2* thl = reinterpret_cast<float2*>(ks + kHeadDim);                 // [64] theta_i/2pi split hi, lo
+  float4* qsl = reinterpret_cast<float4*>(thl + kHalf);                   // [64] (q_i, q_{i+64}, s_i, s_{i+64})
+  double* thd = reinterpret_cast<double*>(qsl + kHalf);                   // [64] theta_i/2pi
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -96,7 +146,7 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   const uint32_t out_off = static_cast<uint32_t>(lane * o_stride);  // outlier entries before this lane's
   const uint32_t second_off = out_off + o_second;
   const uint32_t tile_outs = static_cast<uint32_t>(kTile * o_stride);  // outlier entries of a tile
-  auto load_rec = [&](int s, LutRec<KB>& d) {
+  auto load_rec = [&](int s, LutRec<KB>& d) __attribute__((always_inline)) {
     s = min(s, s_hi - 1);
     const int tile = min(kLutWaves * s + wave, tile_cap);  // wave-uniform
     const size_t tok0 = static_cast<size_t>(tile) * kTile;
@@ -119,46 +169,48 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   };
 
   // ---- set-up inputs, then the first two records ---------------------------------------
-  // Lane l of wave w prepares the table coefficients of one of the eight pairs w + 8 m
-  // whose rows the wave fills, placed for the DPP row broadcasts of the build: 3-bit rows,
-  // m = l & 7 (lane m of every 16-lane row holds pair w + 8 m); 2-bit rows, lane 16 r + f
-  // prepares m = 4 f + r (fill step f finds its row's pair at lane f of the row).
+  // Thread i < 64 stages rotary pair i's query, key scales and frequency in LDS.  Lane l of
+  // wave w distributes the build coefficients of one of the eight pairs w + 8 m whose rows
+  // the wave fills, placed for the DPP row broadcasts of the build: 3-bit rows, m = l & 7
+  // (lane m of every 16-lane row holds pair w + 8 m); 2-bit rows, lane 16 r + f holds
+  // m = 4 f + r (fill step f finds its row's pair at lane f of the row).
   const int P = KB == 3 ? wave + kLutWaves * (lane & 7) : wave + kLutWaves * ((lane >> 4) + 4 * (lane & 1));
-  const bool writes_pab = KB == 3 ? lane < 8 : (lane & 14) == 0;  // one lane per pair
+  const int ip = tid & (kHalf - 1);
   const size_t qbase = (static_cast<size_t>(seq) * a.n_q_heads + kvh) * kHeadDim;
   uint32_t qraw[2];
   if (a.q_is_fp16) {  // wave-uniform; both paths issue the same loads
     const uint16_t* q16 = static_cast<const uint16_t*>(a.q) + qbase;
-    qraw[0] = q16[P];
-    qraw[1] = q16[P + kHalf];
+    qraw[0] = q16[ip];
+    qraw[1] = q16[ip + kHalf];
   } else {
     const uint32_t* q32 = static_cast<const uint32_t*>(a.q) + qbase;
-    qraw[0] = q32[P];
-    qraw[1] = q32[P + kHalf];
+    qraw[0] = q32[ip];
+    qraw[1] = q32[ip + kHalf];
   }
-  const float ks_own = a.k_scale[kvh * kHeadDim + (tid & (kHeadDim - 1))];
+  const float s_ip_lo = a.k_scale[kvh * kHeadDim + ip];
+  const float s_ip_hi = a.k_scale[kvh * kHeadDim + ip + kHalf];
+  const double th_ip = a.theta_rev[ip];
   const uint32_t cb_lane = a.k_cb[lane & (kNc - 1)];
-  const double th_P = a.theta_rev[P];
-  const float2 th_split = make_float2(a.th_hi[lane], a.th_lo[lane]);
 
   LutRec<KB> r0, r1, r2;
   load_rec(s_lo, r0);
   load_rec(s_lo + 1, r1);
 
-  ks[tid & (kHeadDim - 1)] = ks_own;  // threads sharing an entry write the same value
-  thl[lane] = th_split;
-  float qv[2];
+  if (tid < kHalf) {
+    float qv[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) qv[j] = a.q_is_fp16 ? half_bits_to_float(qraw[j]) : __builtin_bit_cast(float, qraw[j]);
+    for (int j = 0; j < 2; ++j) qv[j] = a.q_is_fp16 ? half_bits_to_float(qraw[j]) : __builtin_bit_cast(float, qraw[j]);
+    qsl[tid] = make_float4(qv[0], qv[1], s_ip_lo, s_ip_hi);
+    thd[tid] = th_ip;
+    thl[tid] = make_float2(a.th_hi[tid], a.th_lo[tid]);
+    ks[tid] = s_ip_lo;
+    ks[tid + kHalf] = s_ip_hi;
+  }
   const float zc = zero_code_value<kNc>(cb_lane, lane);  // value every outlier slot decodes to
   // codebook values this lane's table entries use: entry e = a | b << KB
-  float cba[1], cbb;
-  {
-    const int e0 = KB == 3 ? lane : (lane & 15);
-#pragma unroll
-    for (int j = 0; j < 1; ++j) cba[j] = half_bits_to_float(__shfl(static_cast<int>(cb_lane), (e0 + j) & (kNc - 1)) & 0xffffu);
-    cbb = half_bits_to_float(__shfl(static_cast<int>(cb_lane), (e0 >> KB) & (kNc - 1)) & 0xffffu);
-  }
+  const int e0 = KB == 3 ? lane : (lane & 15);
+  const float cba = half_bits_to_float(__shfl(static_cast<int>(cb_lane), e0 & (kNc - 1)) & 0xffffu);
+  const float cbb = half_bits_to_float(__shfl(static_cast<int>(cb_lane), (e0 >> KB) & (kNc - 1)) & 0xffffu);
 
   // E(tau) for all 64 pairs: the argument tau theta_i / 2pi is formed exactly (tau < 512
   // times the 15-bit leading part of theta_i / 2pi) plus the small remainder term.
@@ -170,143 +222,145 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
     er[i] = __builtin_amdgcn_cosf(ph);
     ei[i] = __builtin_amdgcn_sinf(ph);
   }
-  block_lds_barrier();  // ks, thl visible
-  const float sP_lo = ks[P], sP_hi = ks[P + kHalf];
 
-  // ---- table build for super-tile s into buffer b -------------------------------------
-  auto build = [&](int s, int b) {
-    const double t0 = static_cast<double>(s) * (kLutWaves * kTile);
-    float2* T = lut + b * (Sh::kBufBytes / 8);
-    auto coef = [&](double th, float qa, float qb, float s_lo, float s_hi, float4& c, float2& p) {
-      const float r = frac_rev(t0, th);
-      const float cs = __builtin_amdgcn_cosf(r), sn = __builtin_amdgcn_sinf(r);
-      const float pa = qa * cs + qb * sn;  // R(-t0 theta) q
-      const float pb = qb * cs - qa * sn;
-      c = make_float4(s_lo * pa, s_lo * pb, s_hi * pb, -(s_hi * pa));  // alpha, beta, gamma, -delta
-      p = make_float2(pa, pb);
-    };
-    float4 c1;
-    float2 p1;
-    coef(th_P, qv[0], qv[1], sP_lo, sP_hi, c1, p1);
-    if (writes_pab) pab[b * kHalf + P] = p1;
-    static_assert(KB == 2 || KB == 3, "2- and 3-bit keys");
+  // ---- rotated-query coefficients of all 64 pairs for super-tile x (one wave) ---------
+  auto coefs = [&](int x) __attribute__((always_inline)) {
+    const float4 qs = qsl[lane];  // (q_i, q_{i+64}, s_i, s_{i+64}), lane = pair i
+    const double t0 = static_cast<double>(x) * kLutSuper;
+    const float r = frac_rev(t0, thd[lane]);
+    const float cs = __builtin_amdgcn_cosf(r), sn = __builtin_amdgcn_sinf(r);
+    const float pa = qs.x * cs + qs.y * sn;  // R(-t0 theta) q
+    const float pb = qs.y * cs - qs.x * sn;
+    coef[(x & 1) * kHalf + lane] = make_float4(qs.z * pa, qs.z * pb, qs.w * pb, -(qs.w * pa));
+    cpab[(x % 3) * kHalf + lane] = make_float2(pa, pb);
+  };
+
+  // ---- this wave's rows of the table of a super-tile into buffer B ---------------------
+  // cc: the coefficients of pair P (read from LDS before the step's pair loop).
+  auto build = [&](auto bc, float4 cc) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    float2* T = lut + B * (Sh::kBufBytes / 8);
     if constexpr (KB == 3) {
       // wave w fills the rows of pairs w + 8 m, m < 8; lane m of every 16-lane row holds
-      // their coefficients (lane l prepares pair w + 8 (l & 7)) and hands them over by DPP
-      // row broadcast inside the multiplies
-      float4 cc = c1;
-      // at least two wait states between these VALU writes and their DPP reads
-      asm volatile("s_nop 1" : "+v"(cc.x), "+v"(cc.y), "+v"(cc.z), "+v"(cc.w));
+      // their coefficients and hands them over by DPP row broadcast inside the multiplies
+      asm volatile("s_nop 1" : "+v"(cc.x), "+v"(cc.y), "+v"(cc.z), "+v"(cc.w));  // DPP read wait states
       static_for<0, 8>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
-        T[(wave + kLutWaves * m) * kNe + lane] = lut_entry_bcast<m>(cc.x, cc.y, cc.z, cc.w, cba[0], cbb);
+        T[(wave + kLutWaves * m) * kNe + lane] = lut_entry_bcast<m>(cc.x, cc.y, cc.z, cc.w, cba, cbb);
       });
     } else {
       // 16 entries per row: fill step f covers the rows of 4 pairs, m = 4 f + (lane >> 4),
       // whose coefficients lane f of each 16-lane row holds (DPP row broadcast).
-      float4 cc = c1;
-      // at least two wait states between these VALU writes and their DPP reads
-      asm volatile("s_nop 1" : "+v"(cc.x), "+v"(cc.y), "+v"(cc.z), "+v"(cc.w));
+      asm volatile("s_nop 1" : "+v"(cc.x), "+v"(cc.y), "+v"(cc.z), "+v"(cc.w));  // DPP read wait states
       static_for<0, 2>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
         const int i = wave + kLutWaves * (4 * f + (lane >> 4));
-        T[i * kNe + (lane & 15)] = lut_entry_bcast<f>(cc.x, cc.y, cc.z, cc.w, cba[0], cbb);
+        T[i * kNe + (lane & 15)] = lut_entry_bcast<f>(cc.x, cc.y, cc.z, cc.w, cba, cbb);
       });
     }
   };
 
-  // ---- one tile of super-tile s from buffer b ------------------------------------------
-  auto compute = [&](int s, int b, const LutRec<KB>& d) {
-    const uint32_t T = lds_address(lut + b * (Sh::kBufBytes / 8));
-    const unsigned char* lb = lds - lds_address(lds);  // LDS address -> pointer
-    // Software-pipelined over batches of kBatch pairs: the table reads of batch j + 1 are
-    // issued before the FMAs of batch j, so each read's latency is covered by a batch of
-    // arithmetic (the scheduling barriers keep the compiler from re-serializing them).
-    constexpr int kBatch = 8;
+  // Outlier slot operands, requested from LDS before the pair loop.
+  struct OutOps {
+    float dv;      // stored value minus the decoded zero code (0 for an unused slot)
+    float2 th;     // theta/2pi of its pair (hi, lo)
+    float2 p;      // rotated query pair of its pair
+    bool lo_half;  // channel < 64
+  };
+  auto out_ops = [&](uint32_t c, uint32_t vbits, const float2* pab) __attribute__((always_inline)) {
+    OutOps o;
+    const bool used = c != kNoOutlier;  // an unused slot (per-channel rule) adds nothing
+    c &= kHeadDim - 1;                  // a token past the length may hold stale bytes
+    const int i = c & (kHalf - 1);
+    o.dv = used ? half_bits_to_float(vbits) - zc * ks[c] : 0.0f;
+    o.th = thl[i];
+    o.p = pab[i];
+    o.lo_half = c < kHalf;
+    return o;
+  };
+  auto out_term = [&](const OutOps& o) __attribute__((always_inline)) {
+    const float ph = fmaf(tauf, o.th.y, __builtin_amdgcn_fractf(tauf * o.th.x));
+    const float cs = __builtin_amdgcn_cosf(ph), sn = __builtin_amdgcn_sinf(ph);
+    return o.dv * (o.lo_half ? (o.p.x * cs + o.p.y * sn) : (o.p.y * cs - o.p.x * sn));
+  };
+
+  // ---- one tile of super-tile s from table buffer B, and the rows of s + 1 -------------
+  auto step = [&](auto bc, int s, const LutRec<KB>& d, LutRec<KB>& ahead) __attribute__((always_inline)) {
+    constexpr int B = decltype(bc)::value;
+    load_rec(s + 2, ahead);
+    const bool more = s + 1 < s_hi;
+    const float4 cc = coef[((s + 1) & 1) * kHalf + P];  // build coefficients of super-tile s + 1
+    const float2* pab = cpab + (s % 3) * kHalf;
+    OutOps o0, o1;
+    if (kp >= 1) o0 = out_ops(d.oi[0], d.ov[0], pab);
+    if (kp >= 2) o1 = out_ops(d.oi[1], d.ov[1], pab);
+
+    // Rolling window over the 64 pairs: the table read of pair i + kLutAhead is issued
+    // before the FMAs of pair i, so each read has kLutAhead pairs of arithmetic to arrive
+    // in (the scheduling barriers keep that order).
+    const unsigned char* tb = lds + B * Sh::kBufBytes;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float va[2][kBatch], vb[2][kBatch];
-    auto issue = [&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      static_for<0, kBatch>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        constexpr int i = j * kBatch + u;
-        const float2 v = *reinterpret_cast<const float2*>(lb + field_addr<2 * KB, 2 * KB * i, 3>(d.w, T) + i * kNe * 8);
-        va[j & 1][u] = v.x;
-        vb[j & 1][u] = v.y;
-      });
+    float va[kLutAhead + 1], vb[kLutAhead + 1];
+    auto issue = [&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      const float2 v = *reinterpret_cast<const float2*>(tb + i * Sh::kRowBytes + entry_offset<KB, i>(d.w));
+      va[i % (kLutAhead + 1)] = v.x;
+      vb[i % (kLutAhead + 1)] = v.y;
     };
-    auto consume = [&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      static_for<0, kBatch>([&](auto uc) {
-        constexpr int u = decltype(uc)::value;
-        constexpr int i = j * kBatch + u;
-        acc[u & 3] = fmaf(er[i], va[j & 1][u], fmaf(ei[i], vb[j & 1][u], acc[u & 3]));
-      });
-    };
-    issue(std::integral_constant<int, 0>{});
-    static_for<1, kHalf / kBatch>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      issue(jc);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(std::integral_constant<int, j - 1>{});
-      __builtin_amdgcn_sched_barrier(0);
+    static_for<0, kLutAhead>([&](auto ic) { issue(ic); });
+    static_for<0, kHalf>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + kLutAhead < kHalf) issue(std::integral_constant<int, i + kLutAhead>{});
+      acc[i & 3] = fmaf(er[i], va[i % (kLutAhead + 1)], fmaf(ei[i], vb[i % (kLutAhead + 1)], acc[i & 3]));
+      if constexpr ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     });
-    consume(std::integral_constant<int, kHalf / kBatch - 1>{});
     float l = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     // Outliers: the record holds the zero code at each outlier channel; replace its decoded
     // value zc * s_c by the stored fp16 value at the channel's rotated query coefficient.
-    auto add_outlier = [&](uint32_t c, uint32_t vbits) {
-      const bool used = c != kNoOutlier;  // an unused slot (per-channel rule) adds nothing
-      c &= kHeadDim - 1;                  // a token past the length may hold stale bytes
-      const int i = c & (kHalf - 1);
-      const float dv = used ? half_bits_to_float(vbits) - zc * ks[c] : 0.0f;
-      const float2 th = thl[i];
-      const float ph = fmaf(tauf, th.y, __builtin_amdgcn_fractf(tauf * th.x));
-      const float cs = __builtin_amdgcn_cosf(ph), sn = __builtin_amdgcn_sinf(ph);
-      const float2 p = pab[b * kHalf + i];
-      l += dv * (c < kHalf ? (p.x * cs + p.y * sn) : (p.y * cs - p.x * sn));
-    };
-    if (kp >= 1) add_outlier(d.oi[0], d.ov[0]);
-    if (kp >= 2) add_outlier(d.oi[1], d.ov[1]);
+    if (kp >= 1) l += out_term(o0);
+    if (kp >= 2) l += out_term(o1);
     const int t0 = (kLutWaves * s + wave) * kTile;  // wave-uniform
     const int t = t0 + lane;
     if (t < L) {
       if constexpr (kExtra) {
         const size_t o = (stream * S + t) * k;
-        for (int j = kLutPrefetchOutliers; j < k; ++j) add_outlier(a.k_idx[o + j], a.k_val[o + j]);
+        for (int j = kLutPrefetchOutliers; j < k; ++j) l += out_term(out_ops(a.k_idx[o + j], a.k_val[o + j], pab));
       }
       (a.logits + (static_cast<size_t>(seq) * a.n_q_heads + kvh) * S + t0)[lane] = a.sm_scale * l;
     }
+    if (more) build(std::integral_constant<int, B ^ 1>{}, cc);
+    if (wave == s % kLutWaves && s + 2 < s_hi) coefs(s + 2);
+    block_lds_barrier();
   };
 
   // ---- main loop -----------------------------------------------------------------------
-  build(s_lo, 0);
+  block_lds_barrier();  // qsl, thd, ks, thl visible
+  if (wave == 0) coefs(s_lo);
+  if (wave == 1 && s_lo + 1 < s_hi) coefs(s_lo + 1);
+  block_lds_barrier();  // the coefficients of the first two super-tiles visible
+  build(std::integral_constant<int, 0>{}, coef[(s_lo & 1) * kHalf + P]);
   block_lds_barrier();
-  auto step = [&](int s, LutRec<KB>& cur, LutRec<KB>& next2) {
-    const int b = (s - s_lo) & 1;
-    load_rec(s + 2, next2);
-    if (s + 1 < s_hi) build(s + 1, b ^ 1);
-    compute(s, b, cur);
-    block_lds_barrier();
-  };
-  for (int s = s_lo; s < s_hi; s += 3) {
-    step(s, r0, r2);
+  // six steps per round: three record sets (two super-tiles in flight) by two table buffers
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  for (int s = s_lo; s < s_hi; s += 6) {
+    step(I0{}, s, r0, r2);
     if (s + 1 >= s_hi) break;
-    step(s + 1, r1, r0);
+    step(I1{}, s + 1, r1, r0);
     if (s + 2 >= s_hi) break;
-    step(s + 2, r2, r1);
+    step(I0{}, s + 2, r2, r1);
+    if (s + 3 >= s_hi) break;
+    step(I1{}, s + 3, r0, r2);
+    if (s + 4 >= s_hi) break;
+    step(I0{}, s + 4, r1, r0);
+    if (s + 5 >= s_hi) break;
+    step(I1{}, s + 5, r2, r1);
   }
 }
 
 template <int KB, bool kExtra>
 hipError_t launch_qk_lut_t(int batch, const QkArgs& a0, hipStream_t st) {
-  using Sh = LutShape<KB>;
   QkArgs a = a0;
-  const size_t lds = Sh::kBufs * Sh::kBufBytes + kHeadDim * 4 + Sh::kBufs * kHalf * 8 + kHalf * 8;
-  static const bool attr_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&qk_lut_kernel<KB, kExtra>),
-                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                  static_cast<int>(lds)) == hipSuccess;
-  if (!attr_ok) return hipErrorInvalidValue;
   // One resident round: the device's block slots shared equally among the streams, each
   // block walking a contiguous run of super-tiles.
   const int tiles = (a.max_len + kTile - 1) / kTile;
@@ -315,7 +369,7 @@ hipError_t launch_qk_lut_t(int batch, const QkArgs& a0, hipStream_t st) {
   static const int resident = [&] {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&qk_lut_kernel<KB, kExtra>),
-                                                     kLutThreads, lds) != hipSuccess || n < 1)
+                                                     kLutThreads, 0) != hipSuccess || n < 1)
       n = 1;
     return n;
   }();
@@ -323,7 +377,7 @@ hipError_t launch_qk_lut_t(int batch, const QkArgs& a0, hipStream_t st) {
   const long per_stream = std::max(1L, std::min<long>((slots + streams - 1) / streams, supers));
   a.tiles_per_wave = static_cast<int>((supers + per_stream - 1) / per_stream);  // super-tiles per block
   dim3 grid((supers + a.tiles_per_wave - 1) / a.tiles_per_wave, a.n_kv_heads, batch);
-  hipLaunchKernelGGL((qk_lut_kernel<KB, kExtra>), grid, dim3(kLutThreads), lds, st, a);
+  hipLaunchKernelGGL((qk_lut_kernel<KB, kExtra>), grid, dim3(kLutThreads), 0, st, a);
   return hipGetLastError();
 }
 
