@@ -1,10 +1,15 @@
 """Benchmark: quantized-KV decode attention on one MI355X.
 
-A step is one decode step of a whole LLaMA-7B-shaped model at 32K context: for each of
-the model's layers, kvq_quantize_append of the new token's key and value, then
-kvq_qk_matvec and kvq_pv_matvec over that layer's compressed cache.  Every layer has its
-own cache (different seeded inputs), so a step reads ~3.7 GB of compressed KV and no
-layer's cache is still resident in the 256 MB last-level cache when it is read again.
+Default step: one decode step of a whole LLaMA-7B-shaped model (32 layers, 32 heads of
+128) at 1,048,576 tokens of context with 2-bit keys and values and 1 % outliers per
+vector: for each layer, kvq_quantize_append of the new token's key and value (position
+read on the device), then kvq_qk_matvec and kvq_pv_matvec over that layer's compressed
+cache, captured as one HIP graph per step.  All 32 layers stay resident (83.8 GB), so a
+step reads 92 GB and no layer is still in the 256 MB last-level cache when read again.
+
+The same JSON line carries the other decode workloads (the 128K-token 4-bit layer at 0,
+0.5 and 1 % outliers, the batch-16 Llama-3-8B-shaped GQA layer at 64K tokens and the
+32K-token 3-bit layer), measured the same way on a few resident layers each.
 
 Prints ONE JSON line.  value = algorithmic HBM bytes per step / step time (GB/s).
 """
@@ -22,6 +27,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+METRIC = "quantized-KV decode attention: achieved HBM GB/s (% of peak) + KV-tokens/s"
+DTYPE = "f32 (softmax.V dense terms: f16 x f16 products summed in f32)"
+# decode workloads reported beside the headline: name -> (outlier fractions, layers)
+EXTRA = {"llama7b_128k_4bit": ((0.0, 0.005, 0.01), 4), "llama3_8b_gqa_b16_64k": ((None,), 4),
+         "llama7b_32k": ((None,), 32)}
 
 
 def parse():
@@ -29,20 +39,19 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="llama7b_32k")
+    p.add_argument("--workload", default="llama7b_1m_2bit")
     p.add_argument("--outlier-frac", type=float, default=None,
                    help="override the workload's outlier fraction f (k = ceil(f * 128) per vector)")
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the oracle leg (its parity check of a sampled stream and its timing)")
+    p.add_argument("--no-extra", dest="extra", action="store_false",
+                   help="skip the other decode workloads")
     p.add_argument("--no-fp16-baseline", dest="fp16_baseline", action="store_false",
                    help="skip timing the uncompressed fp16 kernels at the same shape")
     p.add_argument("--no-codebook-fit", dest="codebook_fit", action="store_false",
-                   help="skip timing the codebook fit on the layer's key calibration set")
-    p.add_argument("--no-fused", dest="fused", action="store_false",
-                   help="skip timing the single-pass kernel (profiling runs of the two-call path)")
-    p.add_argument("--cpu-heads", type=int, default=32, help="kv-head streams per layer the oracle times in the CPU leg")
-    p.add_argument("--cpu-layers", type=int, default=4, help="layers the oracle times in the CPU leg")
+                   help="skip timing the calibration steps (key scale, key threshold, codebook fit)")
     p.add_argument("--kernel-steps", type=int, default=5,
                    help="rounds of back-to-back launches (one per layer) timed per entry point for the roofline")
     p.add_argument("--traffic-probe", action="store_true",
@@ -62,10 +71,10 @@ def algorithmic_bytes(wl, L):
     q_tok = wl.batch * wl.n_q_heads * L
     qk = tok_heads * (wl.head_dim * wl.k_bits // 8 + 3 * k) + q_tok * 4  # K records + outliers, logits write
     pv = tok_heads * (wl.head_dim * wl.v_bits // 8 + 3 * k + 2) + q_tok * 4  # V tiles + outliers + scale, logits read
-    # append: read 2 fp16 vectors, write one key record, read-modify-write one value tile,
-    # outliers and scale, per (sequence, kv head)
+    # append, per new (sequence, kv head): read the fp16 key and value vectors, write the
+    # key record, the value codes (set in place), both vectors' outliers and the value scale
     nvec = wl.batch * wl.n_kv_heads * wl.n_new
-    app = nvec * (2 * wl.head_dim * 2 + wl.head_dim * wl.k_bits // 8 + 2 * 1024 * wl.v_bits + 6 * k + 2)
+    app = nvec * (2 * wl.head_dim * 2 + wl.head_dim * (wl.k_bits + wl.v_bits) // 8 + 6 * k + 2)
     return qk, pv, app
 
 
@@ -92,22 +101,34 @@ def traffic_from_profile(workload, kernel, src_hash):
 
 
 PROBE_BYTES = 256 << 20  # the calibration kernel reads and writes this many bytes
+KERNEL_SOURCES = {"qk_lut_kernel": ["qk_lut.hip", "kvq_device.h"], "qk_kernel": ["qk.hip", "kvq_device.h"],
+                  "pv_partial_kernel+pv_combine_kernel": ["pv.hip", "kvq_device.h"]}
 
 
 def counter_means(d, counter):
-    """Mean value of `counter` per dispatch, by kernel, from rocprofv3 counter CSVs under d."""
+    """Mean value of `counter` per dispatch, by kernel, from rocprofv3 counter output under
+    d (CSV files or rocpd databases)."""
     import csv
     import glob
     import re
+    import sqlite3
+    pat = re.compile(r"::(qk_lut_kernel|qk_kernel|pv_partial_kernel|pv_combine_kernel|append_kernel)\b|(bitwise_not)")
     acc = {}
+
+    def add(name, value):
+        m = pat.search(name or "")
+        if m:
+            acc.setdefault(m.group(1) or m.group(2), []).append(float(value))
+
     for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
         for row in csv.DictReader(open(f)):
-            if row.get("Counter_Name") != counter:
-                continue
-            m = re.search(r"::(qk_lut_kernel|qk_kernel|pv_partial_kernel|pv_combine_kernel|append_kernel)\b|(bitwise_not)",
-                          row.get("Kernel_Name", ""))
-            if m:
-                acc.setdefault(m.group(1) or m.group(2), []).append(float(row["Counter_Value"]))
+            if row.get("Counter_Name") == counter:
+                add(row.get("Kernel_Name"), row["Counter_Value"])
+    for f in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+        con = sqlite3.connect(f)
+        for name, value in con.execute("select kernel_name, value from counters_collection where counter_name = ?",
+                                       (counter,)):
+            add(name, value)
     return {k: sum(v) / len(v) for k, v in acc.items()}
 
 
@@ -119,11 +140,8 @@ def summarize_counters(fetch_dir, write_dir, workload):
     w_scale = PROBE_BYTES / (write["bitwise_not"] * 1024.0)
     out = {"calibration": {"kernel": "bitwise_not over 256 MiB int32", "fetch_kib": fetch["bitwise_not"],
                            "write_kib": write["bitwise_not"], "fetch_scale": f_scale, "write_scale": w_scale}}
-    groups = {"qk_lut_kernel": (["qk_lut_kernel"], ["qk_lut.hip", "kvq_device.h"]),
-              "qk_kernel": (["qk_kernel"], ["qk.hip", "kvq_device.h"]),
-              "pv_partial_kernel+pv_combine_kernel": (["pv_partial_kernel", "pv_combine_kernel"],
-                                                      ["pv.hip", "kvq_device.h"])}
-    for name, (kerns, src) in groups.items():
+    for name, src in KERNEL_SOURCES.items():
+        kerns = name.split("+")
         if not all(k in fetch and k in write for k in kerns):
             continue
         fk, wk = sum(fetch[k] for k in kerns), sum(write[k] for k in kerns)
@@ -134,8 +152,6 @@ def summarize_counters(fetch_dir, write_dir, workload):
     if os.path.exists(path):
         with open(path) as f:
             allw = json.load(f)
-        if "calibration" in allw:  # single-workload layout of older files
-            allw = {}
     allw[workload] = out
     with open(path, "w") as f:
         json.dump(allw, f, indent=1)
@@ -155,91 +171,101 @@ def cpu_model():
     return platform.processor() or platform.machine()
 
 
-def cpu_baseline(wl, seed, n_streams, n_layers):
-    """Time the oracle (as it stands) on a bounded sample of the same step: the decode-step
-    append and full-length decode attention for n_streams (sequence, kv head) streams of
-    each of n_layers layers, on one thread; report the rate scaled to algorithmic bytes
-    per second."""
-    import torch
-    from threadpoolctl import threadpool_limits
-
-    L = wl.seq_len
-    sm = 1.0 / math.sqrt(wl.head_dim)
-    elapsed = 0.0
-    with threadpool_limits(limits=1):
-        torch.set_num_threads(1)
-        for li in range(n_layers):
-            for i in range(n_streams):
-                elapsed += cpu_stream(wl, seed + li, i, L, sm)
-    return {"value": round(stream_bytes(wl) * n_streams * n_layers / elapsed / 1e9, 6), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{n_streams} of {wl.batch * wl.n_kv_heads} kv-head streams x {n_layers} layers, L={L + 1}: "
-                      f"append of the new token + float64 decode attention, {elapsed:.1f} s, 1 thread, "
-                      f"{cpu_model()}"}
-
-
-def cpu_baseline_parallel(wl, seed, n_streams, n_layers, workers):
-    """The same sample spread over `workers` single-threaded processes (spawned, so they
-    share nothing with this process's GPU state).  Each worker times its streams as the
-    serial leg does; the slowest worker's timed total is the parallel run's time."""
-    import multiprocessing as mp
-
-    L = wl.seq_len
-    sm = 1.0 / math.sqrt(wl.head_dim)
-    tasks = [(wl, seed + li, i, L, sm) for li in range(n_layers) for i in range(n_streams)]
-    ctx = mp.get_context("spawn")
-    with ctx.Pool(workers, initializer=_cpu_worker_init, initargs=(wl, seed, sm)) as pool:
-        timed = pool.starmap(_cpu_worker_task, [(w, tasks[w::workers]) for w in range(workers)])
-    slowest = max(timed)
-    return {"value": round(stream_bytes(wl) * len(tasks) / slowest / 1e9, 6), "unit": "GB/s", "cores": workers,
-            "kind": "oracle",
-            "sample": f"the serial leg's sample over {workers} single-threaded processes: slowest worker "
-                      f"{slowest:.2f} s of timed oracle work (total {sum(timed):.1f} s), {cpu_model()}"}
-
-
-def _cpu_worker_init(wl, seed, sm):
-    from threadpoolctl import threadpool_limits
-    import torch
-    threadpool_limits(limits=1)
-    torch.set_num_threads(1)
-    cpu_stream(wl, seed, 0, 64, sm)  # untimed warm-up of the oracle's code paths
-
-
-def _cpu_worker_task(w, tasks):
-    return sum(cpu_stream(*t) for t in tasks)
-
-
-def stream_bytes(wl):
+def stream_bytes(wl, L):
     """Algorithmic bytes of one (sequence, kv head) stream's share of a decode step."""
-    qk, pv, app = algorithmic_bytes(wl, wl.seq_len + 1)
+    qk, pv, app = algorithmic_bytes(wl, L)
     return (qk + pv + app) / (wl.batch * wl.n_kv_heads)
 
 
-def cpu_stream(wl, seed, i, L, sm):
-    """Oracle seconds for stream i (sequence i // Hkv, kv head i % Hkv) of one layer: the
-    new token's quantization and the decode attention of every query head of its group
-    over all L + 1 tokens (the prefix quantization is not timed)."""
+def cpu_baseline_and_gate(wl, lay, seed, b, h, L0):
+    """The oracle leg, run before the timed region on one sampled (sequence, kv head)
+    stream of the first layer, whose prompt of L0 tokens the GPU has appended:
+      - parity gate: the oracle quantizes the same seeded prompt; the GPU cache must hold
+        the same packed codes, outlier indices/values and value scales bit for bit, and
+        kvq_qk_matvec / kvq_pv_matvec over it must match the oracle's logits and outputs
+        for every query head of the stream's group within the 1e-3 relative criterion
+        (exits non-zero otherwise);
+      - cpu_baseline: the oracle's decode-step work for that stream (quantizing one new
+        token, then float64 decode attention of every query head of the group over the
+        L0 + 1 tokens) timed on one thread, as algorithmic bytes per second (the prompt's
+        quantization is set-up, not timed)."""
     import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
 
+    import long_context_decode_kvq_amd as kvq
     import oracle
     import synth
 
-    b, h = divmod(i, wl.n_kv_heads)
-    ks = synth.key_scale(seed, wl)
-    cbk, cbv = synth.codebook(seed, wl.k_bits, "k"), synth.codebook(seed, wl.v_bits, "v")
-    q = synth.queries(seed, wl)
-    kx = synth.keys(seed, wl, b, h, L + 1).numpy()
-    vx = synth.values(seed, wl, b, h, L + 1).numpy()
-    cache = oracle.quantize_stream(kx[:L], vx[:L], ks[h], cbk, cbv, wl.n_outliers)  # prefix: not timed
-    t0 = time.perf_counter()
-    new = oracle.quantize_stream(kx[L:], vx[L:], ks[h], cbk, cbv, wl.n_outliers)
-    full = oracle.StreamCache(*(np.concatenate([a, b]) for a, b in zip(
-        (cache.k_codes, cache.k_idx, cache.k_val, cache.v_codes, cache.v_idx, cache.v_val, cache.v_scale),
-        (new.k_codes, new.k_idx, new.k_val, new.v_codes, new.v_idx, new.v_val, new.v_scale))))
-    oracle.pack_key_records(new.k_codes, wl.k_bits)
-    for hq in range(h * wl.group, (h + 1) * wl.group):
-        oracle.decode_head(q[b, hq].float().numpy().astype(np.float64), full, ks[h], cbk, cbv, wl.rope_base, sm)
-    return time.perf_counter() - t0
+    c = lay["cache"]
+    cfg = c.cfg
+    sm = 1.0 / math.sqrt(wl.head_dim)
+    ks = lay["k_scale"]
+    cbk, cbv = lay["cbk"], lay["cbv"]
+    t_gate = time.perf_counter()
+    # GPU side: the layer's logits and outputs at the prompt length
+    kvq.qk_matvec(c, lay["q"], lay["bufs"].logits, max_len=L0)
+    kvq.pv_matvec(c, lay["bufs"].logits, lay["bufs"].out, lay["bufs"].workspace, max_len=L0)
+    torch.cuda.synchronize()
+    hq0, hq1 = h * wl.group, (h + 1) * wl.group
+    g_logits = lay["bufs"].logits[b, hq0:hq1, :L0].cpu().numpy()
+    g_out = lay["bufs"].out[b, hq0:hq1].cpu().numpy()
+    g_rec = c.k_records()[b, h, :L0].cpu().numpy()
+    g_tiles = c.v_tiles()[b, h, : (L0 + 63) // 64].cpu().numpy()
+    # the stream as the GPU drew it (the device generator, same length), then on the host:
+    # the prompt and the decode step's first token
+    k16 = synth.keys(seed, wl, b, h, lay["n_all"], "cuda")[:L0 + 1].cpu().numpy()
+    v16 = synth.values(seed, wl, b, h, lay["n_all"], "cuda")[:L0 + 1].cpu().numpy()
+    st = oracle.quantize_stream(k16[:L0], v16[:L0], ks[h], cbk, cbv, wl.n_outliers)
+    codes_ok = np.array_equal(g_rec, oracle.pack_key_records(st.k_codes, wl.k_bits))
+    codes_ok &= np.array_equal(g_tiles, oracle.pack_value_tiles(st.v_codes, wl.v_bits, g_tiles.shape[0] * 64))
+    k = wl.n_outliers
+    if k:
+        for kind, idx, val in (("k", st.k_idx, st.k_val), ("v", st.v_idx, st.v_val)):
+            gi, gv = c.outliers(kind)
+            codes_ok &= np.array_equal(gi[b, h, :L0].cpu().numpy(), idx)
+            codes_ok &= np.array_equal(gv[b, h, :L0].cpu().numpy().view(np.uint16), val)
+    scales = c.v_scale.view(cfg.batch, cfg.n_kv_heads, cfg.max_seq)[b, h, :L0].cpu().numpy().view(np.uint16)
+    codes_ok &= np.array_equal(scales, st.v_scale)
+    worst_l = worst_o = 0.0
+    q = lay["q"]
+    for j, hq in enumerate(range(hq0, hq1)):
+        qh = q[b, hq].float().cpu().numpy().astype(np.float64)
+        ref_l, ref_o = oracle.decode_head(qh, st, ks[h], cbk, cbv, wl.rope_base, sm)
+        tl = oracle.logit_tolerance_scale(qh, st, ks[h], cbk, wl.rope_base, sm)
+        to = oracle.output_tolerance_scale(ref_l, st, cbv)
+        worst_l = max(worst_l, float((np.abs(g_logits[j] - ref_l) / np.maximum(tl, 1e-300)).max()))
+        worst_o = max(worst_o, float((np.abs(g_out[j] - ref_o) / np.maximum(to, 1e-300)).max()))
+    gate = {"layer": 0, "stream": [b, h], "tokens": L0, "codes_bit_exact": bool(codes_ok),
+            "worst_logit_err_over_scale": worst_l, "worst_output_err_over_scale": worst_o, "criterion": 1e-3,
+            "passed": bool(codes_ok and worst_l <= 1e-3 and worst_o <= 1e-3),
+            "seconds": round(time.perf_counter() - t_gate, 1)}
+    if not gate["passed"]:
+        print(json.dumps({"error": "parity gate failed before timing", "parity_gate": gate}), flush=True)
+        sys.exit(3)
+    # the oracle's decode step for this stream, one thread, repeated until about 10 s of work
+    with threadpool_limits(limits=1):
+        torch.set_num_threads(1)
+        t0 = time.perf_counter()
+        reps = 0
+        while reps == 0 or (time.perf_counter() - t0 < 10.0 and reps < 16):
+            new = oracle.quantize_stream(k16[L0:], v16[L0:], ks[h], cbk, cbv, wl.n_outliers)
+            full = oracle.StreamCache(*(np.concatenate([x, y]) for x, y in zip(
+                (st.k_codes, st.k_idx, st.k_val, st.v_codes, st.v_idx, st.v_val, st.v_scale),
+                (new.k_codes, new.k_idx, new.k_val, new.v_codes, new.v_idx, new.v_val, new.v_scale))))
+            oracle.pack_key_records(new.k_codes, wl.k_bits)
+            for hq in range(hq0, hq1):
+                oracle.decode_head(q[b, hq].float().cpu().numpy().astype(np.float64), full, ks[h], cbk, cbv,
+                                   wl.rope_base, sm)
+            reps += 1
+        elapsed = time.perf_counter() - t0
+    torch.set_num_threads(max(1, os.cpu_count() or 1))
+    cpu = {"value": round(reps * stream_bytes(wl, L0 + 1) / elapsed / 1e9, 6), "unit": "GB/s", "cores": 1,
+           "kind": "oracle",
+           "sample": f"1 of {wl.batch * wl.n_kv_heads} (sequence, kv head) streams of one layer, stream {b},{h}, "
+                     f"L={L0 + 1}: quantization of the new token + float64 decode attention of its "
+                     f"{wl.group} query head(s), {reps} times, {elapsed:.1f} s on 1 thread, {cpu_model()}"}
+    return gate, cpu
 
 
 def stream_ceiling(nbytes=1 << 30, reps=10):
@@ -264,15 +290,15 @@ def stream_ceiling(nbytes=1 << 30, reps=10):
             "pct_of_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
 
 
-def key_scale_leg(wl, cfg, seed):
-    """Per-channel key scale over a whole prompt of the workload (the keys a prefill
-    appends), each vector's outliers left out, and the per-channel outlier threshold at a
-    1 % share over the same keys; returns each one's time and bytes read per second."""
+def key_scale_leg(wl, cfg, seed, max_tokens=1 << 20):
+    """Per-channel key scale over a prompt of the workload (the keys a prefill appends),
+    each vector's outliers left out, and the per-channel outlier threshold at a 1 % share
+    over the same keys; returns each one's time and bytes read per second."""
     import torch
 
     import long_context_decode_kvq_amd as kvq
     import synth
-    n = wl.seq_len
+    n = min(wl.seq_len, max_tokens)
     keys = torch.empty(wl.batch, n, wl.n_kv_heads, wl.head_dim, dtype=torch.float16, device="cuda")
     for b in range(wl.batch):
         for h in range(wl.n_kv_heads):
@@ -332,7 +358,7 @@ def codebook_fit_leg(wl, seed, iters=20, n_calib=4096):
             "codebook": [float(x) for x in out.float().cpu()]}
 
 
-def fp16_baseline(wl, cfg, L, kernel_steps, kt, n_layers=4):
+def fp16_baseline(wl, cfg, L, kernel_steps, kt, n_layers):
     """The uncompressed fp16 kernels on the same shape: seeded fp16 caches of n_layers layers
     (each larger than the 256 MB last-level cache), per-launch times measured like the
     compressed kernels', and the compressed path's speed-up over them."""
@@ -376,39 +402,26 @@ def fp16_baseline(wl, cfg, L, kernel_steps, kt, n_layers=4):
             "layers_timed": n_layers, "data": "seeded N(0,1) fp16 keys (as stored after RoPE) and values"}
 
 
-def main():
-    args = parse()
-    if args.summarize_counters:
-        summarize_counters(*args.summarize_counters, args.workload)
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "kvq runs on one GPU; --gpus must be 1 "
-                          "(sharding across GPUs is designed, not built)"}))
-        sys.exit(2)
+def build_layers(wl, n_layers, seed, n_extra, dev="cuda"):
+    """One compressed cache per layer, filled through kvq_quantize_append with the seeded
+    prompt (wl.seq_len tokens per sequence), plus the n_extra decode-step tokens each
+    layer appends later (kept on the device)."""
+    import numpy as np  # noqa: F401
     import torch
 
     import long_context_decode_kvq_amd as kvq
     import synth
-
-    wl = synth.WORKLOADS[args.workload]
-    if args.outlier_frac is not None:
-        wl = wl.with_(outlier_frac=args.outlier_frac)
-    dev = "cuda"
-    kvq.load_library()
     L0 = wl.seq_len
-    total_new = (args.warmup + args.steps + args.kernel_steps) * wl.n_new
-    max_seq = ((L0 + total_new + 63) // 64) * 64
+    max_seq = ((L0 + n_extra * wl.n_new + 63) // 64) * 64
     cfg = kvq.CacheConfig(wl.batch, wl.n_q_heads, wl.n_kv_heads, max_seq, wl.k_bits, wl.v_bits, wl.n_outliers,
                           wl.head_dim, wl.rope_base)
-
-    # ---- build one cache per layer (prefill through kvq_quantize_append) --------------
     layers = []
-    for li in range(args.layers):
-        s = args.seed * 1000 + li
-        ks = torch.from_numpy(synth.key_scale(s, wl))
-        cache = kvq.KVCache(cfg, ks, torch.from_numpy(synth.codebook(s, wl.k_bits, "k")),
-                            torch.from_numpy(synth.codebook(s, wl.v_bits, "v")), dev)
-        n_all = L0 + total_new
+    for li in range(n_layers):
+        s = seed * 1000 + li
+        ks = synth.key_scale(s, wl)
+        cbk, cbv = synth.codebook(s, wl.k_bits, "k"), synth.codebook(s, wl.v_bits, "v")
+        cache = kvq.KVCache(cfg, torch.from_numpy(ks), torch.from_numpy(cbk), torch.from_numpy(cbv), dev)
+        n_all = L0 + n_extra * wl.n_new
         kraw = torch.empty(wl.batch, n_all, wl.n_kv_heads, wl.head_dim, dtype=torch.float16, device=dev)
         vraw = torch.empty_like(kraw)
         for b in range(wl.batch):
@@ -416,15 +429,26 @@ def main():
                 kraw[b, :, h] = synth.keys(s, wl, b, h, n_all, dev)
                 vraw[b, :, h] = synth.values(s, wl, b, h, n_all, dev)
         kvq.quantize_append(cache, kraw[:, :L0].contiguous(), vraw[:, :L0].contiguous())
-        new_k = [kraw[:, L0 + i * wl.n_new: L0 + (i + 1) * wl.n_new].contiguous() for i in range(total_new // wl.n_new)]
-        new_v = [vraw[:, L0 + i * wl.n_new: L0 + (i + 1) * wl.n_new].contiguous() for i in range(total_new // wl.n_new)]
+        # copies (a slice of one token is a contiguous view that would keep the prompt alive)
+        new_k = [kraw[:, L0 + i * wl.n_new: L0 + (i + 1) * wl.n_new].clone() for i in range(n_extra)]
+        new_v = [vraw[:, L0 + i * wl.n_new: L0 + (i + 1) * wl.n_new].clone() for i in range(n_extra)]
         del kraw, vraw
         layers.append(dict(cache=cache, q=synth.queries(s, wl, dev), bufs=kvq.DecodeBuffers(cache),
-                           new_k=new_k, new_v=new_v))
+                           new_k=new_k, new_v=new_v, seed=s, k_scale=ks, cbk=cbk, cbv=cbv, n_all=n_all))
         torch.cuda.synchronize()
+    return layers, cfg, max_seq
 
+
+def run_workload(wl, layers, max_seq, steps, warmup, kernel_steps, graph):
+    """Time `steps` decode steps (after `warmup`), one HIP graph per step: every layer's
+    device-positioned append of the step's token, then q.K^T and softmax.V over the whole
+    capacity bound (kernels read the live length from the device).  Then per-launch times
+    of each entry point over back-to-back launches on the layers, and of the appends."""
+    import torch
+
+    import long_context_decode_kvq_amd as kvq
     ev = lambda: torch.cuda.Event(enable_timing=True)
-    n_graph_steps = args.warmup + args.steps
+    n_graph_steps = warmup + steps
 
     def eager_step(i):
         for lay in layers:
@@ -434,11 +458,8 @@ def main():
             kvq.qk_matvec(c, lay["q"], lay["bufs"].logits, max_len=L)
             kvq.pv_matvec(c, lay["bufs"].logits, lay["bufs"].out, lay["bufs"].workspace, max_len=L)
 
-    # One HIP graph per decode step: every layer's device-positioned append of that
-    # step's new token, then q.K^T and softmax.V over the whole capacity bound (kernels
-    # read the live length from the device).
     graphs = []
-    if args.graph:
+    if graph:
         for i in range(n_graph_steps):
             g = torch.cuda.CUDAGraph()
             saved = [list(l["cache"].lengths) for l in layers]
@@ -454,34 +475,34 @@ def main():
         torch.cuda.synchronize()
 
     def run_step(i):
-        if args.graph:
+        if graph:
             graphs[i].replay()
             for l in layers:
                 l["cache"].lengths = [x + wl.n_new for x in l["cache"].lengths]
         else:
             eager_step(i)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         run_step(i)
     torch.cuda.synchronize()
     start_len = max(layers[0]["cache"].lengths)
     t_start, t_end = ev(), ev()
     w0 = time.perf_counter()
     t_start.record()
-    for i in range(args.steps):
-        run_step(args.warmup + i)
+    for i in range(steps):
+        run_step(warmup + i)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
+    ms_step = t_start.elapsed_time(t_end) / steps
     assert [int(x) for x in layers[0]["cache"].seq_len.cpu()] == layers[0]["cache"].lengths
+    del graphs
 
     # Per-launch kernel durations: HIP events (on the launch stream) around the layers'
     # back-to-back launches of one entry point, so launch overhead overlaps execution.
     L_now = max(layers[0]["cache"].lengths)
     kern_events = {"qk": [], "pv": []}
-    for _ in range(args.kernel_steps):
+    for _ in range(kernel_steps):
         e0, e1, e2 = ev(), ev(), ev()
         e0.record()
         for lay in layers:
@@ -493,29 +514,19 @@ def main():
         kern_events["qk"].append((e0, e1))
         kern_events["pv"].append((e1, e2))
     torch.cuda.synchronize()
-    # the single-pass kernel (one query head per kv head, 2/3-bit keys) on the same layers
-    fused_events = []
-    if args.fused and wl.group == 1 and wl.k_bits <= 3:
-        for _ in range(args.kernel_steps):
-            e0, e1 = ev(), ev()
-            e0.record()
-            for lay in layers:
-                kvq.fused_decode_attention(lay["cache"], lay["q"], lay["bufs"].out, lay["bufs"].workspace, max_len=L_now)
-            e1.record()
-            fused_events.append((e0, e1))
-        torch.cuda.synchronize()
+    n_lay = len(layers)
+    kt = {k: sum(a.elapsed_time(b) for a, b in v) / (len(v) * n_lay) for k, v in kern_events.items()}  # ms/launch
 
     # the decode step's append alone: every layer's device-positioned append of one token
-    # per sequence, back to back (the capacity holds these tokens too)
-    # per decode step (recorded once as a HIP graph when graphs are on, so the host's launch
+    # per sequence (recorded once as a HIP graph when graphs are on, so the host's launch
     # rate does not set the time of these short kernels)
     def appends():
-        for j in range(args.kernel_steps):
+        for j in range(kernel_steps):
             for lay in layers:
                 kvq.quantize_append(lay["cache"], lay["new_k"][n_graph_steps + j], lay["new_v"][n_graph_steps + j],
                                     device_positions=True)
     e0, e1 = ev(), ev()
-    if args.graph:
+    if graph:
         g_app = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_app):
             appends()
@@ -528,87 +539,145 @@ def main():
         appends()
         e1.record()
     torch.cuda.synchronize()
-    app_events = [(e0, e1)]
     for lay in layers:
-        lay["cache"].lengths = [x + wl.n_new * args.kernel_steps for x in lay["cache"].lengths]
-    ceiling = stream_ceiling()
+        lay["cache"].lengths = [x + wl.n_new * kernel_steps for x in lay["cache"].lengths]
+    app_us = 1000 * e0.elapsed_time(e1) / (kernel_steps * n_lay)
+    return dict(ms_step=ms_step, wall=wall, start_len=start_len, L_now=L_now, kt=kt, app_us=app_us)
 
-    # bytes: lengths grow by n_new per step; use the mean length over the timed steps
-    L_mean = start_len + wl.n_new * (args.steps + 1) / 2.0
+
+def summarize(wl, n_layers, r, steps):
+    """GB/s, KV-tokens/s and per-kernel rates of a run_workload result."""
+    L_mean = r["start_len"] + wl.n_new * (steps + 1) / 2.0
     qk_b, pv_b, app_b = algorithmic_bytes(wl, L_mean)
-    step_bytes = args.layers * (qk_b + pv_b + app_b)
-    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    step_bytes = n_layers * (qk_b + pv_b + app_b)
+    gbs = step_bytes / (r["ms_step"] * 1e-3) / 1e9
     # the same without the logits (written by q.K^T, read by softmax.V: 8 bytes per query
-    # head and token), the KV-only figure a single-pass kernel would be judged by
-    kv_only_gbs = (step_bytes - args.layers * 8 * wl.batch * wl.n_q_heads * L_mean) / (ms_step * 1e-3) / 1e9
-    kv_tok_s = args.layers * wl.batch * L_mean / (ms_step * 1e-3)
+    # head and token)
+    kv_only = (step_bytes - n_layers * 8 * wl.batch * wl.n_q_heads * L_mean) / (r["ms_step"] * 1e-3) / 1e9
+    qk_bk, pv_bk, _ = algorithmic_bytes(wl, r["L_now"])
+    kt = r["kt"]
+    return {"ms_per_step": round(r["ms_step"], 4), "gbs": round(gbs, 2), "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "kv_only_gbs": round(kv_only, 1),
+            "kv_tokens_per_s": round(n_layers * wl.batch * L_mean / (r["ms_step"] * 1e-3), 1),
+            "kernel_ms": {k: round(v, 5) for k, v in kt.items()},
+            "kernel_gbs": {"qk": round(qk_bk / (kt["qk"] * 1e-3) / 1e9, 1), "pv": round(pv_bk / (kt["pv"] * 1e-3) / 1e9, 1),
+                           "qk+pv": round((qk_bk + pv_bk) / ((kt["qk"] + kt["pv"]) * 1e-3) / 1e9, 1)},
+            "append_us_per_layer": round(r["app_us"], 2)}
 
-    n_lay = len(layers)
-    kt = {k: sum(a.elapsed_time(b) for a, b in v) / (len(v) * n_lay) for k, v in kern_events.items()}  # ms/launch
-    qk_bk, pv_bk, _ = algorithmic_bytes(wl, L_now)
+
+def workload_config(wl, n_layers):
+    return {"workload": wl.name, "layers": n_layers, "batch": wl.batch, "q_heads": wl.n_q_heads,
+            "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "seq_len": wl.seq_len, "k_bits": wl.k_bits,
+            "v_bits": wl.v_bits, "outliers_per_vector": wl.n_outliers, "new_tokens_per_step": wl.n_new}
+
+
+def main():
+    args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.workload)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1 "
+                          "(sharding across GPUs is described in the design notes, not built)"}))
+        sys.exit(2)
+    import torch
+
+    import long_context_decode_kvq_amd as kvq
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    if args.outlier_frac is not None:
+        wl = wl.with_(outlier_frac=args.outlier_frac)
+    kvq.load_library()
+    n_extra = args.warmup + args.steps + args.kernel_steps
+    t_build = time.perf_counter()
+    layers, cfg, max_seq = build_layers(wl, args.layers, args.seed, n_extra)
+    build_s = time.perf_counter() - t_build
+    free_b, total_b = torch.cuda.mem_get_info()
+    footprint = {"layers": args.layers, "cache_bytes": args.layers * kvq.cache_sizes(cfg).total,
+                 "device_total_bytes": total_b, "device_free_bytes_after_build": free_b,
+                 "build_s": round(build_s, 1)}
+
+    gate = cpu = None
+    if not args.no_cpu_baseline:
+        b_s, h_s = 0, min(9, wl.n_kv_heads - 1)
+        gate, cpu = cpu_baseline_and_gate(wl, layers[0], layers[0]["seed"], b_s, h_s, wl.seq_len)
+
+    r = run_workload(wl, layers, max_seq, args.steps, args.warmup, args.kernel_steps, args.graph)
+    s = summarize(wl, args.layers, r, args.steps)
+    kt = r["kt"]
+    qk_bk, pv_bk, _ = algorithmic_bytes(wl, r["L_now"])
     dom = max(kt, key=kt.get)
     dom_bytes = {"qk": qk_bk, "pv": pv_bk}[dom]
     achieved = dom_bytes / (kt[dom] * 1e-3) / 1e9
-    qk_name, qk_src = (("qk_lut_kernel", "qk_lut.hip") if wl.group == 1 and wl.k_bits <= 3 else ("qk_kernel", "qk.hip"))
+    qk_name = "qk_lut_kernel" if wl.group == 1 and wl.k_bits <= 3 else "qk_kernel"
     dom_name = {"qk": qk_name, "pv": "pv_partial_kernel+pv_combine_kernel"}[dom]
-    src = {"qk": [qk_src, "kvq_device.h"], "pv": ["pv.hip", "kvq_device.h"]}[dom]
     # counted traffic is stored per workload as defined (another outlier count moves other bytes)
-    traffic = traffic_from_profile(args.workload, dom_name, source_hash(src)) if args.outlier_frac is None else None
+    traffic = (traffic_from_profile(args.workload, dom_name, source_hash(KERNEL_SOURCES[dom_name]))
+               if args.outlier_frac is None else None)
+    ceiling = stream_ceiling()
 
     line = {
-        "metric": "quantized-KV decode attention: achieved HBM GB/s (% of peak) + KV-tokens/s",
-        "value": round(gbs, 2),
+        "metric": METRIC,
+        "value": s["gbs"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": s["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic (seeded N(0,1) keys with 4 x10 channels, N(0,1) values; fp16 queries)",
-        "config": {"workload": args.workload, "layers": args.layers, "batch": wl.batch,
-                   "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
-                   "seq_len": wl.seq_len, "k_bits": wl.k_bits, "v_bits": wl.v_bits,
-                   "outliers_per_vector": wl.n_outliers, "new_tokens_per_step": wl.n_new},
-        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "kv_only_gbs": round(kv_only_gbs, 1),
-        "kv_tokens_per_s": round(kv_tok_s, 1),
-        "kernel_ms": {k: round(v, 5) for k, v in kt.items()},
-        "kernel_gbs": {"qk": round(qk_bk / (kt["qk"] * 1e-3) / 1e9, 1),
-                       "pv": round(pv_bk / (kt["pv"] * 1e-3) / 1e9, 1)},
-        "append_us_per_layer": round(1000 * app_events[0][0].elapsed_time(app_events[0][1]) / (args.kernel_steps * n_lay), 2),
+        "dtype": DTYPE,
+        "data": "synthetic (seeded N(0,1) keys with 4 x10 channels per kv head, N(0,1) values; fp16 queries)",
+        "config": workload_config(wl, args.layers),
+        "pct_of_hbm_peak": s["pct_of_hbm_peak"],
+        "kv_only_gbs": s["kv_only_gbs"],
+        "kv_tokens_per_s": s["kv_tokens_per_s"],
+        "kernel_ms": s["kernel_ms"],
+        "kernel_gbs": s["kernel_gbs"],
+        "append_us_per_layer": s["append_us_per_layer"],
+        "footprint": footprint,
         "hbm_read_ceiling": ceiling,
         "graph": bool(args.graph),
-        "wall_s_timed": round(wall, 3),
-        "roofline": {"kernel": dom_name, "launches_timed": args.kernel_steps * n_lay,
+        "wall_s_timed": round(r["wall"], 3),
+        "roofline": {"kernel": dom_name, "launches_timed": args.kernel_steps * args.layers,
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
-    if fused_events:
-        fms = sum(a.elapsed_time(b) for a, b in fused_events) / (len(fused_events) * n_lay)
-        line["fused_single_pass"] = {"ms_per_layer": round(fms, 5), "two_call_ms_per_layer": round(kt["qk"] + kt["pv"], 5),
-                                     "gbs": round((qk_bk + pv_bk - 8 * wl.batch * wl.n_q_heads * L_now) / (fms * 1e-3) / 1e9, 1)}
+    if gate is not None:
+        line["parity_gate"] = gate
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     if args.codebook_fit:
         line["key_scale_calibration"], line["key_threshold_calibration"] = key_scale_leg(wl, cfg, args.seed * 1000 + 7)
         line["codebook_fit"] = codebook_fit_leg(wl, args.seed * 1000)
     if args.fp16_baseline:
-        line["fp16_baseline"] = fp16_baseline(wl, cfg, L_now, args.kernel_steps, kt)
+        n_fp16 = 2 if wl.seq_len * wl.batch * wl.n_kv_heads * 512 > (8 << 30) else 4
+        line["fp16_baseline"] = fp16_baseline(wl, cfg, r["L_now"], args.kernel_steps, kt, n_fp16)
+    del layers
+    torch.cuda.empty_cache()
+    if args.extra:
+        extra = {}
+        for name, (fracs, n_lay) in EXTRA.items():
+            if name == args.workload:
+                continue
+            for f in fracs:
+                w = synth.WORKLOADS[name] if f is None else synth.WORKLOADS[name].with_(outlier_frac=f)
+                e_steps, e_warm, e_ks = 10, 2, 5
+                ls, _, ms = build_layers(w, n_lay, args.seed + 1, e_steps + e_warm + e_ks)
+                rr = run_workload(w, ls, ms, e_steps, e_warm, e_ks, args.graph)
+                entry = {"config": workload_config(w, n_lay), **summarize(w, n_lay, rr, e_steps)}
+                extra[name if f is None else f"{name}@k={w.n_outliers}"] = entry
+                del ls
+                torch.cuda.empty_cache()
+        line["workloads"] = extra
     if args.traffic_probe:
         src_p = torch.ones(PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
         dst_p = torch.empty_like(src_p)
         torch.bitwise_not(src_p, out=dst_p)
         torch.cuda.synchronize()
         del src_p, dst_p
-    if not args.no_cpu_baseline:
-        n_streams = min(args.cpu_heads, wl.batch * wl.n_kv_heads)
-        line["cpu_baseline"] = cpu_baseline(wl, args.seed * 1000, n_streams, args.cpu_layers)
-        # at most 16 worker processes (a host's share per GPU), whatever the host reports
-        workers = max(1, min(16, len(os.sched_getaffinity(0))))
-        if workers > 1:
-            line["cpu_baseline_parallel"] = cpu_baseline_parallel(wl, args.seed * 1000, n_streams, args.cpu_layers,
-                                                                  workers)
     print(json.dumps(line), flush=True)
 
 

@@ -160,7 +160,12 @@ int kvq_qk_matvec(const kvq_shape* shape, const kvq_cache* cache, const void* q,
 
 /*
  * softmax(logits) . V over the compressed value cache plus the value outliers, as a
- * split over the sequence (chunks of tokens) followed by a log-sum-exp combine.
+ * split over the sequence (chunks of tokens) followed by a log-sum-exp combine.  Values
+ * are decoded as the append stored them (summary page, abstract paragraph, techniques
+ * (iii) and (iv); paper note, items (3) and (4)): the per-layer codebook entry of each
+ * code times the vector's own scale (values take the per-token axis, keys the
+ * per-channel one of technique (i)), except at the vector's outlier channels, which take
+ * their stored fp16 values.
  *   logits     float32 [B][Hq][max_seq] as written by kvq_qk_matvec.
  *   out        float32 [B][Hq][D]: sum_t p_t v~[b][h/g][t], p = softmax over t < seq_len[b];
  *              a sequence of length 0 gives zeros.

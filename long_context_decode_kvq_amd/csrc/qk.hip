@@ -447,8 +447,9 @@ hipError_t launch_qk_t(int batch, const QkArgs& a0, hipStream_t s) {
 hipError_t launch_qk(int k_bits, int group, int batch, const QkArgs& a, hipStream_t s) {
 #define KVQ_QK_CASE(KB, G) \
   if (k_bits == KB && group == G) return launch_qk_t<KB, G>(batch, a, s);
-  KVQ_QK_CASE(2, 1) KVQ_QK_CASE(2, 2) KVQ_QK_CASE(2, 4) KVQ_QK_CASE(2, 8)
-  KVQ_QK_CASE(3, 1) KVQ_QK_CASE(3, 2) KVQ_QK_CASE(3, 4) KVQ_QK_CASE(3, 8)
+  // one query head per kv head with 2- or 3-bit keys goes to the table kernel (qk_lut.hip)
+  KVQ_QK_CASE(2, 2) KVQ_QK_CASE(2, 4) KVQ_QK_CASE(2, 8)
+  KVQ_QK_CASE(3, 2) KVQ_QK_CASE(3, 4) KVQ_QK_CASE(3, 8)
   KVQ_QK_CASE(4, 1) KVQ_QK_CASE(4, 2) KVQ_QK_CASE(4, 4) KVQ_QK_CASE(4, 8)
 #undef KVQ_QK_CASE
   return hipErrorInvalidValue;

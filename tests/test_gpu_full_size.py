@@ -96,3 +96,87 @@ def test_full_layer_sampled_heads(name):
                 wf_err = assert_out_close(fused[b, hq].cpu().numpy(), ref_o, scale_o, what=f"{what} hq={hq} single-pass")
                 msg += f", single-pass {wf_err:.2e}"
             print(msg)
+
+
+# single (sequence, kv head) streams: the value pass splits each one into more than 64
+# parts (the combine's register-resident merge holds 64, the rest take its second loop)
+LONG_STREAMS = {"llama7b_128k_4bit": 131072, "llama7b_1m_2bit": 1048576}
+
+
+@pytest.mark.parametrize("name", sorted(LONG_STREAMS))
+def test_long_single_stream_with_positional_values(name):
+    """One long stream whose values are non-negative and code the position (channel 0
+    rises as t / L, channel 1 falls as 1 - t / L, the rest |N(0,1)|), quantized with a
+    non-negative value codebook: the outputs have no cancellation, so the tolerance
+    1e-3 sum_t p_t |v~_t| is a plain relative bound,
+    and a split part dropped, counted twice or merged with the wrong weight moves the
+    position channels by more than it allows."""
+    import long_context_decode_kvq_amd as kvq
+    L = LONG_STREAMS[name]
+    wl = synth.WORKLOADS[name].with_(batch=1, n_q_heads=1, n_kv_heads=1, seq_len=L)
+    seed = 4
+    S = ((L + 63) // 64) * 64
+    cfg = kvq.CacheConfig(1, 1, 1, S, wl.k_bits, wl.v_bits, wl.n_outliers, D, wl.rope_base)
+    ks = synth.key_scale(seed, wl)
+    cbk = synth.codebook(seed, wl.k_bits, "k")
+    # a value codebook of non-negative levels j / (2^b - 1): non-negative values then decode
+    # to non-negative values (the zero code decodes to 0)
+    cbv = np.float16(np.arange(1 << wl.v_bits) / ((1 << wl.v_bits) - 1)).astype(np.float32)
+    cache = kvq.KVCache(cfg, torch.from_numpy(ks), torch.from_numpy(cbk), torch.from_numpy(cbv), "cuda")
+    k16 = synth.keys(seed, wl, 0, 0, L, "cuda")
+    v16 = synth.values(seed, wl, 0, 0, L, "cuda").abs()
+    ramp = torch.arange(L, device="cuda", dtype=torch.float32) / L
+    v16[:, 0] = ramp.half()
+    v16[:, 1] = (1.0 - ramp).half()
+    kvq.quantize_append(cache, k16[None, :, None].contiguous(), v16[None, :, None].contiguous())
+    q = synth.queries(seed, wl, "cuda").contiguous()
+    bufs = kvq.DecodeBuffers(cache)
+    kvq.qk_matvec(cache, q, bufs.logits, max_len=S)
+    kvq.pv_matvec(cache, bufs.logits, bufs.out, bufs.workspace, max_len=S)
+    torch.cuda.synchronize()
+    # with one stream the value pass splits it into min(block slots, ceil(tiles / 16)) parts,
+    # at least 256 block slots on this device: more than 64 parts for both lengths
+    assert -(-L // (64 * 16)) > 64
+    c = oracle.quantize_stream(k16.cpu().numpy(), v16.cpu().numpy(), ks[0], cbk, cbv, wl.n_outliers)
+    qh = q[0, 0].float().cpu().numpy().astype(np.float64)
+    sm = 1.0 / math.sqrt(D)
+    ref_l, ref_o = oracle.decode_head(qh, c, ks[0], cbk, cbv, wl.rope_base, sm)
+    scale_l = oracle.logit_tolerance_scale(qh, c, ks[0], cbk, wl.rope_base, sm)
+    assert_logits_close(bufs.logits[0, 0, :L].cpu().numpy(), ref_l, scale_l, what=name)
+    got = bufs.out[0, 0].cpu().numpy().astype(np.float64)
+    assert np.all(ref_o >= 0)
+    scale_o = oracle.output_tolerance_scale(ref_l, c, cbv)
+    assert np.allclose(scale_o, ref_o, rtol=1e-12, atol=0)  # no cancellation: the two bounds coincide
+    err = np.abs(got - ref_o)
+    assert np.all(err <= 1e-3 * ref_o), f"{name}: worst relative output error {(err / ref_o).max():.3g}"
+    print(f"{name}: worst relative output error {(err / ref_o).max():.2e}, "
+          f"position channels {got[0]:.6f} / {got[1]:.6f}")
+
+
+def test_32_layer_1m_cache_is_resident():
+    """The full 32-layer cache of the 1M-token 2-bit LLaMA-7B-shaped model (k = 2) fits
+    on the device: every layer's buffers allocated at once, sized by kvq_cache_sizes."""
+    import long_context_decode_kvq_amd as kvq
+    wl = synth.WORKLOADS["llama7b_1m_2bit"]
+    S = wl.capacity
+    cfg = kvq.CacheConfig(wl.batch, wl.n_q_heads, wl.n_kv_heads, S, wl.k_bits, wl.v_bits, wl.n_outliers, D,
+                          wl.rope_base)
+    per_layer = kvq.cache_sizes(cfg).total
+    torch.cuda.empty_cache()
+    free0, total = torch.cuda.mem_get_info()
+    ks = torch.ones(wl.n_kv_heads, D)
+    cbk, cbv = torch.from_numpy(synth.codebook(0, 2, "k")), torch.from_numpy(synth.codebook(0, 2, "v"))
+    layers = [kvq.KVCache(cfg, ks, cbk, cbv, "cuda") for _ in range(32)]
+    torch.cuda.synchronize()
+    held = sum(sum(t.numel() * t.element_size() for t in (c.k_codes, c.v_codes, c.k_out_idx, c.k_out_val,
+                                                            c.v_out_idx, c.v_out_val, c.v_scale, c.k_scale,
+                                                            c.k_codebook, c.v_codebook, c.seq_len))
+               for c in layers)
+    free1, _ = torch.cuda.mem_get_info()
+    print(f"32 layers x {per_layer / 1e9:.3f} GB = {held / 1e9:.2f} GB held; device {total / 1e9:.1f} GB, "
+          f"free {free0 / 1e9:.1f} GB before, {free1 / 1e9:.1f} GB after")
+    assert held == 32 * per_layer
+    assert 83e9 < held < 85e9
+    assert free0 - free1 >= held
+    del layers
+    torch.cuda.empty_cache()

@@ -35,6 +35,7 @@ CASES = {
     "mha4_4bit_k0": (_wl("llama7b_128k_4bit", n_q_heads=4, n_kv_heads=4, seq_len=1100, outlier_frac=0.0),
                      [1100], None),
     "mha4_2bit": (_wl("llama7b_1m_2bit", n_q_heads=4, n_kv_heads=4, seq_len=2100), [2100], None),
+    "mha2_2bit_k1": (_wl("llama7b_1m_2bit", n_q_heads=2, n_kv_heads=2, seq_len=1500, outlier_frac=0.005), [1500], None),
     "gqa_ragged_batch": (_wl("llama3_8b_gqa_b16_64k", batch=3, n_q_heads=8, n_kv_heads=2, seq_len=1300),
                          [1300, 517, 1], None),
     "gqa_g8": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=8, n_kv_heads=1, seq_len=700), [700, 64], None),
@@ -55,6 +56,21 @@ CASES = {
                   [800, 391], None),
     "gqa8_2bit": (_wl("llama3_8b_gqa_b16_64k", batch=1, n_q_heads=8, n_kv_heads=1, seq_len=1000, k_bits=2, v_bits=2),
                   [1000], None),
+    # every (bits, group) instantiation the C ABI accepts: 4-bit keys with grouped heads,
+    # 2-bit keys at g = 4, 2- and 4-bit values with grouped heads
+    "gqa2_4bit": (_wl("llama7b_128k_4bit", batch=2, n_q_heads=4, n_kv_heads=2, seq_len=700), [700, 333], None),
+    "gqa4_4bitk_2bitv": (_wl("llama7b_128k_4bit", batch=1, n_q_heads=8, n_kv_heads=2, seq_len=900, v_bits=2),
+                         [900], None),
+    "gqa8_4bit": (_wl("llama7b_128k_4bit", batch=1, n_q_heads=8, n_kv_heads=1, seq_len=1000), [1000], None),
+    "gqa4_2bitk_4bitv": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=8, n_kv_heads=2, seq_len=800, k_bits=2,
+                              v_bits=4), [800, 65], None),
+    "gqa2_3bitk_2bitv": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=4, n_kv_heads=2, seq_len=600, v_bits=2),
+                         [600, 129], None),
+    # one query head per kv head with the remaining (key, value) bit widths of the
+    # single-pass kernel
+    "mha2_k2v3": (_wl("llama7b_32k", n_q_heads=2, n_kv_heads=2, seq_len=900, k_bits=2, v_bits=3), [900], None),
+    "mha2_k3v2": (_wl("llama7b_32k", n_q_heads=2, n_kv_heads=2, seq_len=900, k_bits=3, v_bits=2), [900], None),
+    "mha2_k3v4": (_wl("llama7b_32k", n_q_heads=2, n_kv_heads=2, seq_len=900, k_bits=3, v_bits=4), [900], None),
     # the per-channel key outlier rule (key_outliers = 1): the frozen key scale is a
     # per-channel quantile of |key| over the calibration draw and doubles as the threshold
     "pc_mha4_3bit_k2": (_wl("llama7b_32k", n_q_heads=4, n_kv_heads=4, seq_len=1100), [1100], None),
