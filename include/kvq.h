@@ -175,6 +175,22 @@ int kvq_pv_matvec(const kvq_shape* shape, const kvq_cache* cache, const float* l
                   void* workspace, size_t workspace_bytes, int32_t max_len, hipStream_t stream);
 
 /*
+ * kvq_pv_matvec without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Arguments and results as for kvq_pv_matvec; the split partials go to a
+ * device array of the library of KVQ_NOALLOC_SCRATCH_BYTES bytes (each device holds its
+ * own copy until the process ends; the call itself allocates nothing).
+ * Errors: as kvq_pv_matvec, and KVQ_ERR_WORKSPACE when kvq_workspace_bytes(shape, max_len)
+ * exceeds KVQ_NOALLOC_SCRATCH_BYTES (for example 32 query heads of one sequence up to
+ * about 2M tokens, or 16 sequences of 32 query heads up to about 126K tokens).  All calls
+ * on one device share the array: calls that overlap on one device (several streams, or
+ * several threads) race and must be serialised by the caller.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+int kvq_pv_matvec_noalloc(const kvq_shape* shape, const kvq_cache* cache, const float* logits, float* out,
+                          int32_t max_len, hipStream_t stream);
+
+/*
  * Single-pass decode attention: kvq_qk_matvec followed by kvq_pv_matvec in one kernel
  * pass (plus the combine), without writing the logits (summary page, abstract paragraph:
  * decode is bandwidth-bound, and the logits are the one intermediate both passes move).

@@ -22,7 +22,7 @@ KVQ_OK = 0
 STATUS_NAMES = {0: "KVQ_OK", -1: "KVQ_ERR_INVALID", -2: "KVQ_ERR_UNSUPPORTED",
                 -3: "KVQ_ERR_CAPACITY", -4: "KVQ_ERR_WORKSPACE", -5: "KVQ_ERR_HIP"}
 EXPORTED = ("kvq_cache_sizes", "kvq_workspace_bytes", "kvq_quantize_append", "kvq_qk_matvec",
-            "kvq_pv_matvec", "kvq_decode_attention", "kvq_key_scale", "kvq_key_threshold_workspace_bytes",
+            "kvq_pv_matvec", "kvq_pv_matvec_noalloc", "kvq_decode_attention", "kvq_key_scale", "kvq_key_threshold_workspace_bytes",
             "kvq_key_threshold", "kvq_fit_workspace_bytes", "kvq_fit_codebook", "kvq_stream_read",
             "kvq_fp16_qk_matvec", "kvq_fp16_pv_matvec", "kvq_status_string",
             "kvq_abi_version")
@@ -80,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_pv_matvec.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(CacheDesc), P, P, P, SZ,
                                   I32, P]
     lib.kvq_pv_matvec.restype = ctypes.c_int
+    lib.kvq_pv_matvec_noalloc.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(CacheDesc), P, P, I32, P]
+    lib.kvq_pv_matvec_noalloc.restype = ctypes.c_int
     lib.kvq_decode_attention.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(CacheDesc), P, I32, ctypes.c_float,
                                          P, P, SZ, I32, P]
     lib.kvq_decode_attention.restype = ctypes.c_int
@@ -265,6 +267,22 @@ def pv_matvec(cache: KVCache, logits: torch.Tensor, out: torch.Tensor, workspace
                                       logits.data_ptr(), out.data_ptr(), workspace.data_ptr(),
                                       workspace.numel() * workspace.element_size(), ml, _stream(stream))
     _check("kvq_pv_matvec", st)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # KVQ_NOALLOC_SCRATCH_BYTES
+
+
+def pv_matvec_noalloc(cache: KVCache, logits: torch.Tensor, out: torch.Tensor, max_len: int | None = None,
+                      stream=None):
+    """kvq_pv_matvec_noalloc: kvq_pv_matvec with the split partials in the library's own
+    device array (no workspace; calls overlapping on one device race)."""
+    cfg = cache.cfg
+    assert out.dtype == torch.float32 and out.numel() == cfg.batch * cfg.n_q_heads * cfg.head_dim
+    assert logits.dtype == torch.float32 and out.is_contiguous()
+    ml = max(max(cache.lengths), 1) if max_len is None else int(max_len)
+    st = load_library().kvq_pv_matvec_noalloc(ctypes.byref(cache._shape), ctypes.byref(cache._desc),
+                                              logits.data_ptr(), out.data_ptr(), ml, _stream(stream))
+    _check("kvq_pv_matvec_noalloc", st)
 
 
 def fused_decode_attention(cache: KVCache, q: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,

@@ -4,8 +4,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -40,6 +42,31 @@ int check_cache_common(const kvq_shape* s, const kvq_cache* c) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+// Split partials of kvq_pv_matvec_noalloc: a device array of the library, so that the call
+// allocates nothing.  Each device holds its own copy at its own address, found once per
+// device with hipGetSymbolAddress (host code never passes the array's name itself).
+__device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+std::mutex scratch_mu;
+
+// The current device's address of `scratch`.
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVQ_ERR_HIP;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVQ_ERR_HIP;
+      scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return KVQ_OK;
+}
 
 size_t n_chunks_for(int32_t max_len) { return (static_cast<size_t>(max_len) + kvq::kPvChunk - 1) / kvq::kPvChunk; }
 
@@ -243,6 +270,22 @@ int kvq_pv_matvec(const kvq_shape* s, const kvq_cache* c, const float* logits, f
   if (max_len < 1 || max_len > s->max_seq) return KVQ_ERR_INVALID;
   if (!workspace || workspace_bytes < kvq_workspace_bytes(s, max_len)) return KVQ_ERR_WORKSPACE;
   const kvq::PvArgs a = make_pv_args(s, c, logits, out, workspace, max_len);
+  return hip_status(kvq::launch_pv(s->v_bits, s->n_q_heads / s->n_kv_heads, s->batch, a, stream));
+}
+
+int kvq_pv_matvec_noalloc(const kvq_shape* s, const kvq_cache* c, const float* logits, float* out, int32_t max_len,
+                          hipStream_t stream) {
+  int st = check_shape(s);
+  if (st != KVQ_OK) return st;
+  st = check_cache_common(s, c);
+  if (st != KVQ_OK) return st;
+  if (!c->v_codes || !c->v_scale || !c->v_codebook || !logits || !out) return KVQ_ERR_INVALID;
+  if (max_len < 1 || max_len > s->max_seq) return KVQ_ERR_INVALID;
+  if (kvq_workspace_bytes(s, max_len) > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != KVQ_OK) return st;
+  const kvq::PvArgs a = make_pv_args(s, c, logits, out, ws, max_len);
   return hip_status(kvq::launch_pv(s->v_bits, s->n_q_heads / s->n_kv_heads, s->batch, a, stream));
 }
 

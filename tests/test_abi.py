@@ -182,3 +182,25 @@ def test_stream_read_rejects_before_launch():
     assert lib.kvq_stream_read(4104, 160, 4096, None) == -1      # misaligned buffer
     assert lib.kvq_stream_read(None, 160, 4096, None) == -1      # no buffer
     assert lib.kvq_stream_read(4096, 160, None, None) == -1      # no sink
+
+
+def test_noalloc_value_pass_rejects_before_launch():
+    """kvq_pv_matvec_noalloc checks its arguments like kvq_pv_matvec and refuses sizes whose
+    split partials exceed its fixed device array, before touching the device."""
+    lib = kvq.load_library()
+    p = 4096  # fake device pointers, never dereferenced
+    fake = kvq.CacheDesc(*([ctypes.c_void_p(p)] * len(kvq.CacheDesc._fields_)))
+    f = lib.kvq_pv_matvec_noalloc
+    shape = cfg().shape()
+    assert f(ctypes.byref(shape), None, p, p, 10, None) == -1                    # no cache
+    assert f(ctypes.byref(shape), ctypes.byref(fake), None, p, 10, None) == -1   # no logits
+    assert f(ctypes.byref(shape), ctypes.byref(fake), p, None, 10, None) == -1   # no output
+    assert f(ctypes.byref(shape), ctypes.byref(fake), p, p, 0, None) == -1       # empty bound
+    assert f(ctypes.byref(shape), ctypes.byref(fake), p, p, 257, None) == -1     # beyond capacity
+    assert f(ctypes.byref(cfg(head_dim=64).shape()), ctypes.byref(fake), p, p, 10, None) == -2
+    # 32 query heads of one sequence: partials of ceil(L / 1024) parts of 130 floats each
+    limit = kvq.NOALLOC_SCRATCH_BYTES
+    fits = 1024 * (limit // (32 * 130 * 4))             # the longest bound that fits
+    big = cfg(batch=1, n_q_heads=32, n_kv_heads=32, max_seq=fits + 1024).shape()
+    assert kvq.workspace_bytes(cfg(batch=1, n_q_heads=32, n_kv_heads=32, max_seq=fits + 1024), fits) <= limit
+    assert f(ctypes.byref(big), ctypes.byref(fake), p, p, fits + 1, None) == -4
