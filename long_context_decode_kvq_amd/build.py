@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["append.hip", "qk.hip", "qk_lut.hip", "pv.hip", "fused.hip", "fp16_baseline.hip", "codebook_fit.hip", "key_scale.hip", "key_threshold.hip", "stream_read.hip", "kvq_api.cpp"]
+SOURCES = ["append.hip", "qk.hip", "qk_lut.hip", "qk_mfma.hip", "pv.hip", "fused.hip", "fp16_baseline.hip", "codebook_fit.hip", "key_scale.hip", "key_threshold.hip", "stream_read.hip", "kvq_api.cpp"]
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 VALU forms are switched off for every device pass.

@@ -45,6 +45,34 @@ __device__ __forceinline__ float2 lut_entry_bcast(float al, float be, float ga, 
   return make_float2(A, B);
 }
 
+// Byte offset of rotary pair I's entry in a table row of 8-byte entries indexed by the
+// pair's 2KB-bit code field (a | b << KB): the field times 8, by a shift and a mask
+// (single-rate VOP2 operations; a field that straddles two words takes an align-bit
+// first).  W is the token's key record.
+template <int KB, int I, int N>
+__device__ __forceinline__ uint32_t pair_entry_offset(const uint32_t (&w)[N]) {
+  constexpr int kBits = 2 * KB;
+  constexpr int pos = kBits * I;
+  constexpr int wi = pos / 32;
+  constexpr int sh = pos % 32;
+  constexpr uint32_t mask = ((1u << kBits) - 1u) << 3;
+  static_assert(wi < N, "field outside the record");
+  uint32_t r;
+  if constexpr (sh + kBits <= 32) {
+    if constexpr (sh >= 3) {
+      asm("v_lshrrev_b32_e32 %0, %2, %1\n\tv_and_b32_e32 %0, %3, %0" : "=&v"(r) : "v"(w[wi]), "n"(sh - 3), "n"(mask));
+    } else {
+      asm("v_lshlrev_b32_e32 %0, %2, %1\n\tv_and_b32_e32 %0, %3, %0" : "=&v"(r) : "v"(w[wi]), "n"(3 - sh), "n"(mask));
+    }
+  } else {
+    static_assert(wi + 1 < N, "straddling field outside the record");
+    asm("v_alignbit_b32 %0, %1, %2, %3\n\tv_and_b32_e32 %0, %4, %0"
+        : "=&v"(r)
+        : "v"(w[wi + 1]), "v"(w[wi]), "n"(sh - 3), "n"(mask));
+  }
+  return r;
+}
+
 // Wave reductions: four DPP steps combine the 16 lanes of each row (xor 1, xor 2, half-row
 // mirror, row mirror), then the four row results are read into scalar registers.  Every
 // lane gets the result; no LDS round trips.

@@ -92,6 +92,8 @@ inline int blocks_per_cu(const void* kernel, int threads) {
 hipError_t launch_append(int k_bits, int v_bits, const AppendArgs& a, hipStream_t s);
 hipError_t launch_qk(int k_bits, int group, int batch, const QkArgs& a, hipStream_t s);
 hipError_t launch_qk_lut(int k_bits, int batch, const QkArgs& a, hipStream_t s);
+// 2/3-bit keys, 2, 4 or 8 query heads per kv head: the head contraction on the matrix cores.
+hipError_t launch_qk_mfma(int k_bits, int group, int batch, const QkArgs& a, hipStream_t s);
 hipError_t launch_pv(int v_bits, int group, int batch, const PvArgs& a, hipStream_t s);
 // Log-sum-exp merge of the (o, m, l) partials in a.partial into a.out (used by launch_pv).
 hipError_t launch_pv_combine(int batch, const PvArgs& a, hipStream_t s);

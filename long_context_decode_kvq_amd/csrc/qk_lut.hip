@@ -49,7 +49,6 @@ struct LutShape {
   static constexpr int kNe = kNc * kNc;               // code pairs (a | b << KB) per rotary pair
   static constexpr int kRowBytes = kNe * 8;           // (A, B) float pairs of one rotary pair
   static constexpr int kBufBytes = kHalf * kRowBytes; // 64 rows
-  static constexpr uint32_t kMask = (kNe - 1) << 3;   // code field times 8
   // tables, build coefficients, rotated-query pairs, key scales, frequencies (split and
   // float64), query and scales per pair
   static constexpr int kLdsBytes = 2 * kBufBytes + 2 * kHalf * 16 + 3 * kHalf * 8 + kHeadDim * 4 + kHalf * 8 +
@@ -61,33 +60,6 @@ struct LutRec {
   uint32_t w[4 * KB];     // the token's key record
   uint32_t oi[2], ov[2];  // its first two outliers: channels and fp16 value bits
 };
-
-// Byte offset of pair I's (A, B) entry within its table row: its 2KB-bit code field
-// times 8, by a shift and a mask (single-rate VOP2 operations; a field that straddles two
-// words takes an align-bit first).
-template <int KB, int I, int N>
-__device__ __forceinline__ uint32_t entry_offset(const uint32_t (&w)[N]) {
-  constexpr int kBits = 2 * KB;
-  constexpr int pos = kBits * I;
-  constexpr int wi = pos / 32;
-  constexpr int sh = pos % 32;
-  constexpr uint32_t mask = LutShape<KB>::kMask;
-  static_assert(wi < N, "field outside the record");
-  uint32_t r;
-  if constexpr (sh + kBits <= 32) {
-    if constexpr (sh >= 3) {
-      asm("v_lshrrev_b32_e32 %0, %2, %1\n\tv_and_b32_e32 %0, %3, %0" : "=&v"(r) : "v"(w[wi]), "n"(sh - 3), "n"(mask));
-    } else {
-      asm("v_lshlrev_b32_e32 %0, %2, %1\n\tv_and_b32_e32 %0, %3, %0" : "=&v"(r) : "v"(w[wi]), "n"(3 - sh), "n"(mask));
-    }
-  } else {
-    static_assert(wi + 1 < N, "straddling field outside the record");
-    asm("v_alignbit_b32 %0, %1, %2, %3\n\tv_and_b32_e32 %0, %4, %0"
-        : "=&v"(r)
-        : "v"(w[wi + 1]), "v"(w[wi]), "n"(sh - 3), "n"(mask));
-  }
-  return r;
-}
 
 // kExtra: outliers beyond the first kLutPrefetchOutliers per token exist (read in a loop
 // of their own); without them that loop is compiled out.
@@ -303,7 +275,7 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
     float va[kLutAhead + 1], vb[kLutAhead + 1];
     auto issue = [&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      const float2 v = *reinterpret_cast<const float2*>(tb + i * Sh::kRowBytes + entry_offset<KB, i>(d.w));
+      const float2 v = *reinterpret_cast<const float2*>(tb + i * Sh::kRowBytes + pair_entry_offset<KB, i>(d.w));
       va[i % (kLutAhead + 1)] = v.x;
       vb[i % (kLutAhead + 1)] = v.y;
     };

@@ -66,6 +66,13 @@ CASES = {
                               v_bits=4), [800, 65], None),
     "gqa2_3bitk_2bitv": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=4, n_kv_heads=2, seq_len=600, v_bits=2),
                          [600, 129], None),
+    # fp32 queries with grouped heads (the matrix-core kernel's two-part fp16 split)
+    "gqa4_3bit_q32": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=8, n_kv_heads=2, seq_len=700, q_dtype="fp32"),
+                      [700, 190], None),
+    "gqa8_2bit_q32": (_wl("llama3_8b_gqa_b16_64k", batch=1, n_q_heads=8, n_kv_heads=1, seq_len=600, k_bits=2,
+                          q_dtype="fp32"), [600], None),
+    "gqa2_2bit_q32": (_wl("llama3_8b_gqa_b16_64k", batch=1, n_q_heads=4, n_kv_heads=2, seq_len=555, k_bits=2,
+                          q_dtype="fp32"), [555], None),
     # one query head per kv head with the remaining (key, value) bit widths of the
     # single-pass kernel
     "mha2_k2v3": (_wl("llama7b_32k", n_q_heads=2, n_kv_heads=2, seq_len=900, k_bits=2, v_bits=3), [900], None),
@@ -146,6 +153,27 @@ def test_qk_and_pv_parity(built):
             scale_o = oracle.output_tolerance_scale(ref_l, c, case.cbv)
             worst_o = max(worst_o, assert_out_close(out[b, hq], ref_o, scale_o, what=f"{name} b={b} hq={hq}"))
     print(f"{name}: worst logit rel err {worst_l:.2e}, worst output rel err {worst_o:.2e}")
+
+
+@pytest.mark.parametrize("q_log2", [-40, 40])
+@pytest.mark.parametrize("k_bits", [2, 3])
+def test_grouped_fp32_query_magnitudes(q_log2, k_bits):
+    """fp32 queries far outside fp16's range (|q| near 2^42 or 2^-38) with grouped heads:
+    the per-head power-of-two prescale before the two-part fp16 split keeps every logit
+    within the tolerance (outputs are not compared: at 2^40 the softmax is a one-hot of
+    logits whose tolerance exceeds their gaps)."""
+    wl = _wl("llama3_8b_gqa_b16_64k", batch=1, n_q_heads=8, n_kv_heads=2, seq_len=300, k_bits=k_bits, q_dtype="fp32")
+    case = make_case("q_magnitude", wl, [300])
+    case.q = case.q * (2.0 ** q_log2)
+    cache = case.build_gpu()
+    logits, _ = _run_decode(case, cache)
+    sm = 1.0 / math.sqrt(D)
+    for hq in range(wl.n_q_heads):
+        h = hq // wl.group
+        c = case.oracle_stream(0, h)
+        ref_l, _ = case.oracle_decode(0, hq)
+        scale_l = oracle.logit_tolerance_scale(case.q_head(0, hq), c, case.ks[h], case.cbk, wl.rope_base, sm)
+        assert_logits_close(logits[0, hq, :300], ref_l, scale_l, what=f"q 2^{q_log2} k_bits={k_bits} hq={hq}")
 
 
 def test_fused_decode_matches_oracle(built):
