@@ -14,8 +14,10 @@
 //     p_t = exp(l_t - m), w_t = p_t * s_t, and the outlier corrections
 //     p_t * (x_c - zc * s_t) are added into the wave's own LDS row of channels;
 //   * lane = channel pair (2l, 2l+1): the 2b-bit field holding two consecutive tokens of
-//     one channel indexes a small table of fp16 pairs (cb[a], cb[b]); w_t reaches every
-//     lane as a scalar operand (read from lane t) of a mixed-precision FMA.
+//     one channel indexes a small table of fp16 pairs (cb[a], cb[b]).  With one query head
+//     w_t reaches every lane as a scalar operand (read from lane t) of a packed fp16 dot
+//     product; with several, the fp16 weights of 4 heads are the A operand and the fp16
+//     codebook values of 4 tokens of a channel the B operand of v_mfma_f32_4x4x4_16b_f16.
 // The four waves merge their states once at the end; each block writes one (o, m, l).
 // pv_combine: one block per (sequence, query head) merges the block partials.
 #include <algorithm>
@@ -26,6 +28,9 @@
 
 namespace kvq {
 namespace {
+
+typedef _Float16 pv_half4 __attribute__((ext_vector_type(4)));
+typedef float pv_float4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
@@ -62,7 +67,14 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   // With several query heads the tile's fp16 weight pairs are staged in LDS and read back
   // at wave-uniform addresses (broadcast), four pairs per read, instead of one lane read
   // (a VALU instruction) per pair and head; with one head the lane reads measured faster.
-  constexpr bool kStageW = G > 1;
+  // Several query heads: the dense part runs on the matrix cores, with this wave's fp16
+  // weights staged in LDS as [head][token] rows (rows past G stay zero).  With one head the
+  // packed dot products measured faster (1M 2-bit layer: 294 against 353 us; 128K 4-bit:
+  // 74 against 83 us): three of the four MFMA rows would carry nothing.
+  constexpr bool kMfma = G > 1;
+  constexpr int kGroups = G > 4 ? G / 4 : 1;
+  __shared__ _Float16 wsh[kMfma ? kWaves : 1][kMfma ? 4 * kGroups : 1][kMfma ? kTile : 1];
+  constexpr bool kStageW = G > 1 && !kMfma;
   __shared__ uint4 wst[kStageW ? kWaves : 1][G][kTile / 8];  // (w_2m, w_2m+1) at word m
 
   const int tid = threadIdx.x;
@@ -156,6 +168,9 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   for (int e = tid; e < kWaves * G * kHeadDim; e += kThreads) {
     (&osp[0][0][0])[e] = 0.0f;
     (&osi[0][0][0])[e] = 0;
+  }
+  if constexpr (kMfma) {
+    for (int e = tid; e < kWaves * 4 * kGroups * kTile; e += kThreads) (&wsh[0][0][0])[e] = static_cast<_Float16>(0.0f);
   }
   const float zc = zero_code_value<kNc>(cb_lo, lane);  // value every outlier slot decodes to
   block_lds_barrier();
@@ -251,74 +266,127 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
         *cell = make_int2(0, 0);
       }
     }
-    // Dense part: lane = channel pair.  The token weights enter as fp16 pairs (w_t, w_t+1),
-    // one scalar operand per two tokens of a packed dot product with the fp16 codebook pair
-    // (cb[a], cb[b]) (both products exact in fp32, fp32 accumulation).  Each tile's weights
-    // are scaled by 2^sh, which puts the tile's largest weight in [2^13, 2^14): every weight
-    // whose rounding matters is then a normal fp16 number, so its relative error is at most
-    // 2^-11 and the output's at most 2^-11 sum_t p_t |v~_t,c|; 2^-sh is undone exactly after
-    // the tile.
-    float unsc[G];
-    uint32_t wpair[G];
+    // Dense part: lane = channel pair, the token weights in fp16 against fp16 codebook
+    // values (products exact in fp32, fp32 accumulation).  Each tile's weights are scaled by
+    // 2^sh, which puts the tile's largest weight in [2^13, 2^14): every weight whose rounding
+    // matters is then a normal fp16 number, so its relative error is at most 2^-11 and the
+    // output's at most 2^-11 sum_t p_t |v~_t,c|; 2^-sh is undone exactly after the tile.
+    if constexpr (kMfma) {
+      // Dense part on the matrix cores: v_mfma_f32_4x4x4_16b_f16 with the tile's fp16
+      // weights of 4 heads as the A operand (row m = head, the same in all 16 blocks, read
+      // back from this wave's LDS rows) and the fp16 codebook values of 4 consecutive tokens
+      // of one channel as the B operand (block b, column n = lane 4b + n: channel 2l + half
+      // of lane l), so one MFMA adds 4 tokens of 64 channels for 4 heads and lane l ends
+      // with o[h][2l + half] in row h of its result.  Weights are prescaled per tile and
+      // head as in the packed-dot path (largest in [2^13, 2^14), relative rounding error
+      // at most 2^-11).
+      float unsc[G];
+      _Float16* wrow = &wsh[kMfma ? wave : 0][0][0];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float wmax = wave_max_f32(wts[h]);
-      const int ex = wmax > 0.0f ? static_cast<int>((__builtin_bit_cast(uint32_t, wmax) >> 23) & 0xffu) - 127 : 0;
-      const int sh = min(max(13 - ex, -100), 100);  // 2^sh * wmax in [2^13, 2^14)
-      unsc[h] = __builtin_bit_cast(float, static_cast<uint32_t>(127 - sh) << 23);
-      const float ws = wts[h] * __builtin_bit_cast(float, static_cast<uint32_t>(127 + sh) << 23);
-      const uint32_t wh = __builtin_bit_cast(uint16_t, static_cast<_Float16>(ws));
-      const uint32_t wn = dpp_u32<0xF5>(wh);  // quad_perm [1,1,3,3]: lane 2m gets lane 2m + 1
-      wpair[h] = wh | (wn << 16);             // in lane 2m: (w_2m, w_2m+1)
-      if (kStageW && (lane & 1) == 0) reinterpret_cast<uint32_t*>(&wst[kStageW ? wave : 0][h][0])[lane >> 1] = wpair[h];
-    }
-    if constexpr (kStageW) wave_lds_sync();
-    // the weight pair of tokens (2m, 2m + 1) for head h, the same in every lane
-    auto wpair_of = [&](int h, auto mc) {
-      constexpr int m = decltype(mc)::value;
-      if constexpr (kStageW) {
-        const uint4 wq = wst[kStageW ? wave : 0][h][m / 4];
-        return (m & 3) == 0 ? wq.x : (m & 3) == 1 ? wq.y : (m & 3) == 2 ? wq.z : wq.w;
-      } else {
-        return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wpair[h]), 2 * m));
+      for (int h = 0; h < G; ++h) {
+        const float wmax = wave_max_f32(wts[h]);
+        const int ex = wmax > 0.0f ? static_cast<int>((__builtin_bit_cast(uint32_t, wmax) >> 23) & 0xffu) - 127 : 0;
+        const int sh = min(max(13 - ex, -100), 100);  // 2^sh * wmax in [2^13, 2^14)
+        unsc[h] = __builtin_bit_cast(float, static_cast<uint32_t>(127 - sh) << 23);
+        wrow[h * kTile + lane] = static_cast<_Float16>(wts[h] * __builtin_bit_cast(float, static_cast<uint32_t>(127 + sh) << 23));
       }
-    };
-    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-    float accp[G][2][2];
+      wave_lds_sync();
+      const unsigned char* wa = reinterpret_cast<const unsigned char*>(wrow) + (lane & 3) * (kTile * 2);
+      pv_float4 dacc[kGroups][2];
 #pragma unroll
-    for (int h = 0; h < G; ++h) accp[h][0][0] = accp[h][0][1] = accp[h][1][0] = accp[h][1][1] = 0.0f;
-    if constexpr (kQuad) {
-      static_for<0, kTile / 4>([&](auto qc) {
-        constexpr int qq = decltype(qc)::value;
-        const uint2 e0 = lut4[field<4 * VB, 4 * VB * qq>(d.w)];
-        const uint2 e1 = lut4[field<4 * VB, kChanBits + 4 * VB * qq>(d.w)];
+      for (int g = 0; g < kGroups; ++g) dacc[g][0] = dacc[g][1] = pv_float4{0.0f, 0.0f, 0.0f, 0.0f};
+      static_for<0, kTile / 4>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        uint2 bq[2];
+        if constexpr (kQuad) {
+          bq[0] = lut4[field<4 * VB, 4 * VB * j>(d.w)];
+          bq[1] = lut4[field<4 * VB, kChanBits + 4 * VB * j>(d.w)];
+        } else {
+          bq[0] = make_uint2(lut2[field<2 * VB, 4 * VB * j>(d.w)], lut2[field<2 * VB, 4 * VB * j + 2 * VB>(d.w)]);
+          bq[1] = make_uint2(lut2[field<2 * VB, kChanBits + 4 * VB * j>(d.w)],
+                             lut2[field<2 * VB, kChanBits + 4 * VB * j + 2 * VB>(d.w)]);
+        }
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const half2_t wlo = __builtin_bit_cast(half2_t, wpair_of(h, std::integral_constant<int, 2 * qq>{}));
-          const half2_t whi = __builtin_bit_cast(half2_t, wpair_of(h, std::integral_constant<int, 2 * qq + 1>{}));
-          accp[h][0][0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e0.x), wlo, accp[h][0][0], false);
-          accp[h][0][1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e0.y), whi, accp[h][0][1], false);
-          accp[h][1][0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e1.x), wlo, accp[h][1][0], false);
-          accp[h][1][1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e1.y), whi, accp[h][1][1], false);
+        for (int g = 0; g < kGroups; ++g) {
+          const uint2 aw = *reinterpret_cast<const uint2*>(wa + g * (4 * kTile * 2) + j * 8);
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            dacc[g][hf] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(pv_half4, aw), __builtin_bit_cast(pv_half4, bq[hf]),
+                                                             dacc[g][hf], 0, 0, 0);
+            asm volatile("" : "+a"(dacc[g][hf]));  // keeps each product next to its operands
+          }
         }
       });
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        acc[h][0] = fmaf(dacc[h >> 2][0][h & 3], unsc[h], acc[h][0]);
+        acc[h][1] = fmaf(dacc[h >> 2][1][h & 3], unsc[h], acc[h][1]);
+      }
     } else {
-      static_for<0, kTile / 2>([&](auto mc) {
-        constexpr int mm = decltype(mc)::value;
-        const half2_t e0 = __builtin_bit_cast(half2_t, lut2[field<2 * VB, 2 * VB * mm>(d.w)]);
-        const half2_t e1 = __builtin_bit_cast(half2_t, lut2[field<2 * VB, kChanBits + 2 * VB * mm>(d.w)]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const half2_t wp = __builtin_bit_cast(half2_t, wpair_of(h, mc));
-          accp[h][0][mm & 1] = __builtin_amdgcn_fdot2(e0, wp, accp[h][0][mm & 1], false);
-          accp[h][1][mm & 1] = __builtin_amdgcn_fdot2(e1, wp, accp[h][1][mm & 1], false);
+      // One head: the weights enter as fp16 pairs (w_t, w_t+1), one scalar operand per two
+      // tokens of a packed dot product with the fp16 codebook pair (cb[a], cb[b]).
+      float unsc[G];
+      uint32_t wpair[G];
+  #pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float wmax = wave_max_f32(wts[h]);
+        const int ex = wmax > 0.0f ? static_cast<int>((__builtin_bit_cast(uint32_t, wmax) >> 23) & 0xffu) - 127 : 0;
+        const int sh = min(max(13 - ex, -100), 100);  // 2^sh * wmax in [2^13, 2^14)
+        unsc[h] = __builtin_bit_cast(float, static_cast<uint32_t>(127 - sh) << 23);
+        const float ws = wts[h] * __builtin_bit_cast(float, static_cast<uint32_t>(127 + sh) << 23);
+        const uint32_t wh = __builtin_bit_cast(uint16_t, static_cast<_Float16>(ws));
+        const uint32_t wn = dpp_u32<0xF5>(wh);  // quad_perm [1,1,3,3]: lane 2m gets lane 2m + 1
+        wpair[h] = wh | (wn << 16);             // in lane 2m: (w_2m, w_2m+1)
+        if (kStageW && (lane & 1) == 0) reinterpret_cast<uint32_t*>(&wst[kStageW ? wave : 0][h][0])[lane >> 1] = wpair[h];
+      }
+      if constexpr (kStageW) wave_lds_sync();
+      // the weight pair of tokens (2m, 2m + 1) for head h, the same in every lane
+      auto wpair_of = [&](int h, auto mc) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (kStageW) {
+          const uint4 wq = wst[kStageW ? wave : 0][h][m / 4];
+          return (m & 3) == 0 ? wq.x : (m & 3) == 1 ? wq.y : (m & 3) == 2 ? wq.z : wq.w;
+        } else {
+          return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(wpair[h]), 2 * m));
         }
-      });
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      acc[h][0] = fmaf(accp[h][0][0] + accp[h][0][1], unsc[h], acc[h][0]);
-      acc[h][1] = fmaf(accp[h][1][0] + accp[h][1][1], unsc[h], acc[h][1]);
+      };
+      typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+      float accp[G][2][2];
+  #pragma unroll
+      for (int h = 0; h < G; ++h) accp[h][0][0] = accp[h][0][1] = accp[h][1][0] = accp[h][1][1] = 0.0f;
+      if constexpr (kQuad) {
+        static_for<0, kTile / 4>([&](auto qc) {
+          constexpr int qq = decltype(qc)::value;
+          const uint2 e0 = lut4[field<4 * VB, 4 * VB * qq>(d.w)];
+          const uint2 e1 = lut4[field<4 * VB, kChanBits + 4 * VB * qq>(d.w)];
+  #pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const half2_t wlo = __builtin_bit_cast(half2_t, wpair_of(h, std::integral_constant<int, 2 * qq>{}));
+            const half2_t whi = __builtin_bit_cast(half2_t, wpair_of(h, std::integral_constant<int, 2 * qq + 1>{}));
+            accp[h][0][0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e0.x), wlo, accp[h][0][0], false);
+            accp[h][0][1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e0.y), whi, accp[h][0][1], false);
+            accp[h][1][0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e1.x), wlo, accp[h][1][0], false);
+            accp[h][1][1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e1.y), whi, accp[h][1][1], false);
+          }
+        });
+      } else {
+        static_for<0, kTile / 2>([&](auto mc) {
+          constexpr int mm = decltype(mc)::value;
+          const half2_t e0 = __builtin_bit_cast(half2_t, lut2[field<2 * VB, 2 * VB * mm>(d.w)]);
+          const half2_t e1 = __builtin_bit_cast(half2_t, lut2[field<2 * VB, kChanBits + 2 * VB * mm>(d.w)]);
+  #pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const half2_t wp = __builtin_bit_cast(half2_t, wpair_of(h, mc));
+            accp[h][0][mm & 1] = __builtin_amdgcn_fdot2(e0, wp, accp[h][0][mm & 1], false);
+            accp[h][1][mm & 1] = __builtin_amdgcn_fdot2(e1, wp, accp[h][1][mm & 1], false);
+          }
+        });
+      }
+  #pragma unroll
+      for (int h = 0; h < G; ++h) {
+        acc[h][0] = fmaf(accp[h][0][0] + accp[h][0][1], unsc[h], acc[h][0]);
+        acc[h][1] = fmaf(accp[h][1][0] + accp[h][1][1], unsc[h], acc[h][1]);
+      }
     }
     wave_lds_sync();  // the cleared cells are written before the next tile's atomics
   };
