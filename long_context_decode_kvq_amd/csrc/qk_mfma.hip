@@ -242,14 +242,17 @@ __global__ __launch_bounds__(kMfThreads) void qk_mfma_kernel(QkArgs a) {
   const float cbb = half_bits_to_float(__shfl(static_cast<int>(cb_lane), (e0 >> KB) & (kNc - 1)) & 0xffffu);
 
   // E(tau) for all 64 pairs: the argument tau theta_i / 2pi is formed exactly (tau < 512
-  // times the 15-bit leading part of theta_i / 2pi) plus the small remainder term.
-  float er[kHalf], ei[kHalf];
+  // times the 15-bit leading part of theta_i / 2pi) plus the small remainder term.  The
+  // sine is kept negated, so that both products of the rotation are plain two-operand
+  // multiplies (the other sign rides on the mixed FMA's operand modifier).
+  float er[kHalf], en[kHalf];
   const float tauf = static_cast<float>(tau);
 #pragma unroll
   for (int i = 0; i < kHalf; ++i) {
     const float ph = fmaf(tauf, a.th_lo[i], __builtin_amdgcn_fractf(tauf * a.th_hi[i]));
     er[i] = __builtin_amdgcn_cosf(ph);
-    ei[i] = __builtin_amdgcn_sinf(ph);
+    en[i] = -__builtin_amdgcn_sinf(ph);
+    asm volatile("" : "+v"(en[i]));  // stored negated: the compiler would fold the sign back
   }
 
   // ---- table coefficients and rotated query pairs of super-tile x (one wave, lane = pair) -
@@ -294,6 +297,9 @@ __global__ __launch_bounds__(kMfThreads) void qk_mfma_kernel(QkArgs a) {
     int i;         // its pair
     bool lo_half;  // channel < 64
   };
+  // Channel c of pair i rotated by tau theta_i meets the rotated query pair (p_a, p_b) as
+  // p_a cos + p_b sin (c = i) or p_b cos - p_a sin (c = i + 64): both are p_a u + p_b v
+  // with (u, v) chosen once per outlier and scaled by its value, two FMAs per head.
   auto out_ops = [&](uint32_t c, uint32_t vbits) __attribute__((always_inline)) {
     OutOps o;
     const bool used = c != kNoOutlier;  // an unused slot (per-channel rule) adds nothing
@@ -307,10 +313,12 @@ __global__ __launch_bounds__(kMfThreads) void qk_mfma_kernel(QkArgs a) {
   auto out_add = [&](const OutOps& o, const float2* pab, float (&ol)[G]) __attribute__((always_inline)) {
     const float ph = fmaf(tauf, o.th.y, __builtin_amdgcn_fractf(tauf * o.th.x));
     const float cs = __builtin_amdgcn_cosf(ph), sn = __builtin_amdgcn_sinf(ph);
+    const float u = o.dv * (o.lo_half ? cs : -sn);
+    const float v = o.dv * (o.lo_half ? sn : cs);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float2 p = pab[h * kHalf + o.i];
-      ol[h] = fmaf(o.dv, o.lo_half ? (p.x * cs + p.y * sn) : (p.y * cs - p.x * sn), ol[h]);
+      ol[h] = fmaf(p.x, u, fmaf(p.y, v, ol[h]));
     }
   };
 
@@ -348,8 +356,8 @@ __global__ __launch_bounds__(kMfThreads) void qk_mfma_kernel(QkArgs a) {
       constexpr int i = decltype(ic)::value;
       if constexpr (i + kMfAhead < kHalf) issue(std::integral_constant<int, i + kMfAhead>{});
       const float xa = va[i % (kMfAhead + 1)], xb = vb[i % (kMfAhead + 1)];
-      const float ya = fmaf(xa, er[i], -(xb * ei[i]));
-      const float yb = fmaf(xa, ei[i], xb * er[i]);
+      const float ya = fmaf(xa, er[i], xb * en[i]);
+      const float yb = fmaf(xa, -en[i], xb * er[i]);
       hp[i & 1] = __builtin_bit_cast(uint32_t, mf_half2{static_cast<_Float16>(ya), static_cast<_Float16>(yb)});
       if constexpr ((i & 1) == 1) {
         constexpr int j = i >> 1;
