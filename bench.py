@@ -102,6 +102,7 @@ def traffic_from_profile(workload, kernel, src_hash):
 
 PROBE_BYTES = 256 << 20  # the calibration kernel reads and writes this many bytes
 KERNEL_SOURCES = {"qk_lut_kernel": ["qk_lut.hip", "kvq_device.h"], "qk_kernel": ["qk.hip", "kvq_device.h"],
+                  "qk_mfma_kernel": ["qk_mfma.hip", "kvq_device.h"],
                   "pv_partial_kernel+pv_combine_kernel": ["pv.hip", "kvq_device.h"]}
 
 
@@ -112,7 +113,8 @@ def counter_means(d, counter):
     import glob
     import re
     import sqlite3
-    pat = re.compile(r"::(qk_lut_kernel|qk_kernel|pv_partial_kernel|pv_combine_kernel|append_kernel)\b|(bitwise_not)")
+    pat = re.compile(r"::(qk_lut_kernel|qk_mfma_kernel|qk_kernel|pv_partial_kernel|pv_combine_kernel|append_kernel)\b"
+                     r"|(bitwise_not)")
     acc = {}
 
     def add(name, value):
@@ -610,7 +612,7 @@ def main():
     dom = max(kt, key=kt.get)
     dom_bytes = {"qk": qk_bk, "pv": pv_bk}[dom]
     achieved = dom_bytes / (kt[dom] * 1e-3) / 1e9
-    qk_name = "qk_lut_kernel" if wl.group == 1 and wl.k_bits <= 3 else "qk_kernel"
+    qk_name = ("qk_kernel" if wl.k_bits == 4 else "qk_lut_kernel" if wl.group == 1 else "qk_mfma_kernel")
     dom_name = {"qk": qk_name, "pv": "pv_partial_kernel+pv_combine_kernel"}[dom]
     # counted traffic is stored per workload as defined (another outlier count moves other bytes)
     traffic = (traffic_from_profile(args.workload, dom_name, source_hash(KERNEL_SOURCES[dom_name]))

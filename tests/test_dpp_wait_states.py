@@ -6,7 +6,14 @@ coefficients, wave maxima), where the compiler's hazard recognizer cannot see th
 the required wait states are written by hand (s_nop).  This test compiles every kernel
 source to assembly (no GPU needed) and scans each DPP instruction backwards: a VALU
 instruction writing its first source operand (the one DPP swizzles) must be at least two
-wait states earlier (s_nop N counts N + 1, any other instruction one)."""
+wait states earlier (s_nop N counts N + 1, any other instruction one).
+
+A second check covers the other way an inline-asm instruction escapes the compiler's
+hazard model: an instruction whose result a following VALU instruction must not read too
+soon (measured on gfx950: a VALU copy of a v_dot2c_f32_f16 result read within two wait
+states gets the old value, at four the new one).  The compiler spaces such reads after the
+dot, matrix and transcendental instructions it emits itself, but not after ones written
+inside an asm statement, so none of those may appear in inline asm."""
 import os
 import re
 import shutil
@@ -76,3 +83,31 @@ def test_dpp_reads_wait_two_states(src, tmp_path):
     assert r.returncode == 0, r.stderr[-2000:]
     total, found = dpp_hazards(open(out).read().splitlines())
     assert not found, f"{src}: {len(found)} DPP reads too soon after a VALU write of their source: {found[:3]}"
+
+
+# instruction families whose results need wait states before a VALU read, handled by the
+# compiler for its own instructions only
+_SLOW_RESULT = re.compile(r"\bv_(dot\d|mfma|smfmac|exp|log|rcp|rsq|sqrt|sin|cos)\w*")
+_ASM_STRING = re.compile(r"\basm\s*(?:volatile\s*)?\(((?:\s*\"(?:[^\"\\]|\\.)*\")+)")
+
+
+def slow_result_asm(text):
+    """Mnemonics of dot, matrix or transcendental instructions written in inline asm."""
+    found = []
+    for m in _ASM_STRING.finditer(text):
+        found += _SLOW_RESULT.findall(m.group(1))
+    return found
+
+
+def test_slow_result_scanner_flags_planted_asm():
+    planted = 'asm("v_dot2c_f32_f16_dpp %0, %1, %2 row_newbcast:3" : "+v"(a) : "v"(w), "v"(e));\n' \
+              'asm volatile("s_nop 4\\n\\t"\n "v_exp_f32 %0, %1" : "=v"(x) : "v"(y));\n' \
+              'asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:1" : "=v"(p) : "v"(a), "v"(b));\n' \
+              'x = __builtin_amdgcn_fdot2(a, b, c, false);'
+    assert slow_result_asm(planted) == ["dot2", "exp"]
+
+
+@pytest.mark.parametrize("src", sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h", ".cpp"))))
+def test_no_slow_result_instruction_in_inline_asm(src):
+    found = slow_result_asm(open(os.path.join(CSRC, src)).read())
+    assert not found, f"{src}: dot/matrix/transcendental instructions in inline asm: {found}"
