@@ -73,6 +73,13 @@ CASES = {
                           q_dtype="fp32"), [600], None),
     "gqa2_2bit_q32": (_wl("llama3_8b_gqa_b16_64k", batch=1, n_q_heads=4, n_kv_heads=2, seq_len=555, k_bits=2,
                           q_dtype="fp32"), [555], None),
+    # grouped heads on the matrix cores without outliers, with one, and with a sequence of
+    # one token beside a ragged one
+    "gqa4_3bit_k0": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=8, n_kv_heads=2, seq_len=640, outlier_frac=0.0),
+                     [640, 100], None),
+    "gqa8_2bit_k1": (_wl("llama3_8b_gqa_b16_64k", batch=1, n_q_heads=8, n_kv_heads=1, seq_len=777, k_bits=2, v_bits=2,
+                         outlier_frac=0.005), [777], None),
+    "gqa2_len1": (_wl("llama3_8b_gqa_b16_64k", batch=3, n_q_heads=4, n_kv_heads=2, seq_len=65), [1, 65, 2], None),
     # one query head per kv head with the remaining (key, value) bit widths of the
     # single-pass kernel
     "mha2_k2v3": (_wl("llama7b_32k", n_q_heads=2, n_kv_heads=2, seq_len=900, k_bits=2, v_bits=3), [900], None),
