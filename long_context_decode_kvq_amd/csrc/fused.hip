@@ -67,8 +67,7 @@ __global__ __launch_bounds__(kFuseThreads) void fused_decode_kernel(QkArgs a, Pv
   float2* thl = pab + 2 * kHalf;                                        // [64] theta_i/2pi split hi, lo
   uint32_t* lut2 = reinterpret_cast<uint32_t*>(thl + kHalf);            // fp16 (cb[a], cb[b]) per token pair
   int* osi = reinterpret_cast<int*>(lut2 + kPairEntries);               // [8][128] fixed-point outlier sums
-  float* osp = reinterpret_cast<float*>(osi + kFuseWaves * kHeadDim);   // [8][128] further outliers
-  float* wo = osp + kFuseWaves * kHeadDim;                              // [8][128] per-wave sums
+  float* wo = reinterpret_cast<float*>(osi + kFuseWaves * kHeadDim);    // [8][128] per-wave sums
   float* wml = wo + kFuseWaves * kHeadDim;                              // [8][2] per-wave max, sum
 
   const int tid = threadIdx.x;
@@ -173,10 +172,7 @@ __global__ __launch_bounds__(kFuseThreads) void fused_decode_kernel(QkArgs a, Pv
   ks[tid & (kHeadDim - 1)] = ks_own;  // threads sharing an entry write the same value
   thl[lane] = th_split;
   lut2[tid & (kPairEntries - 1)] = vcb_a | (vcb_b << 16);
-  for (int e = tid; e < kFuseWaves * kHeadDim; e += kFuseThreads) {
-    osi[e] = 0;
-    osp[e] = 0.0f;
-  }
+  for (int e = tid; e < kFuseWaves * kHeadDim; e += kFuseThreads) osi[e] = 0;
   float qv[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) qv[j] = a.q_is_fp16 ? half_bits_to_float(qraw[j]) : __builtin_bit_cast(float, qraw[j]);
@@ -301,7 +297,6 @@ __global__ __launch_bounds__(kFuseThreads) void fused_decode_kernel(QkArgs a, Pv
   // ---- softmax . V of this wave's tile, running state per wave --------------------------
   float m_run = -INFINITY, lsum = 0.0f, acc0 = 0.0f, acc1 = 0.0f;
   int* my_osi = osi + wave * kHeadDim;
-  float* my_osp = osp + wave * kHeadDim;
   auto accumulate = [&](int s, float lg, const ValRec<VB>& d) {
     const int t = (kFuseWaves * s + wave) * kTile + lane;
     const bool valid = t < L;
@@ -313,24 +308,29 @@ __global__ __launch_bounds__(kFuseThreads) void fused_decode_kernel(QkArgs a, Pv
       acc0 *= sc;
       acc1 *= sc;
       lsum *= sc;
-      my_osp[2 * lane] *= sc;
-      my_osp[2 * lane + 1] *= sc;
     }
     const float pr = valid ? __expf(lg - m_run) : 0.0f;  // hardware exp2 of x log2(e): relative error < 4e-6 for x >= -100
     lsum += pr;
     const float wts = pr * sv;
     wave_lds_sync();
-    // Value outliers: channel c gets p_t (x_c - zv s_t); the first two of each token are
-    // summed in 32-bit fixed point (scale 2^(23 - e), 2^e above the tile's largest term)
-    // with integer atomics, further ones with float atomics.
+    // Value outliers: channel c gets p_t (x_c - zv s_t), summed in 32-bit fixed point with
+    // integer atomics (scale 2^(23 - e), 2^e above the tile's largest term over all of the
+    // token's outliers; at most one term per channel and token, so the sums fit and do not
+    // depend on the order the atomics land).  Outliers past the first two are read twice,
+    // for the scale and for the sums.
     float unscale = 0.0f;
     bool have_fixed = false;
     {
       const float dv0 = half_bits_to_float(d.ov[0]) - zv * sv;
       const float dv1 = half_bits_to_float(d.ov[1]) - zv * sv;
       const int c0 = d.oi[0] & (kHeadDim - 1), c1 = d.oi[1] & (kHeadDim - 1);  // stale bytes past the length
-      const float mloc = pr * fmaxf(kp >= 1 ? fabsf(dv0) : 0.0f, kp >= 2 ? fabsf(dv1) : 0.0f);
-      const float m = wave_max_f32(mloc);
+      const bool more = k > kFuseOutliers && valid;
+      const size_t slot = (stream * S + t) * k;
+      float dmax = fmaxf(kp >= 1 ? fabsf(dv0) : 0.0f, kp >= 2 ? fabsf(dv1) : 0.0f);
+      if (more) {
+        for (int j = kFuseOutliers; j < k; ++j) dmax = fmaxf(dmax, fabsf(half_bits_to_float(pa.v_val[slot + j]) - zv * sv));
+      }
+      const float m = wave_max_f32(pr * dmax);
       have_fixed = m > 0.0f;  // wave-uniform
       if (have_fixed) {
         const int e = min(max(static_cast<int>((__builtin_bit_cast(uint32_t, m) >> 23) & 0xffu) - 126, -100), 100);
@@ -338,14 +338,13 @@ __global__ __launch_bounds__(kFuseThreads) void fused_decode_kernel(QkArgs a, Pv
         unscale = __builtin_bit_cast(float, static_cast<uint32_t>(e - 23 + 127) << 23);       // 2^(e-23)
         if (kp >= 1) atomicAdd(my_osi + c0, static_cast<int>(rintf(pr * dv0 * sc)));
         if (kp >= 2) atomicAdd(my_osi + c1, static_cast<int>(rintf(pr * dv1 * sc)));
-      }
-    }
-    if (k > kFuseOutliers && valid) {
-      const size_t slot = stream * S + t;
-      for (int j = kFuseOutliers; j < k; ++j) {
-        const int c = pa.v_idx[slot * k + j] & (kHeadDim - 1);
-        const float dv = half_bits_to_float(pa.v_val[slot * k + j]) - zv * sv;
-        atomicAdd(my_osp + c, pr * dv);
+        if (more) {
+          for (int j = kFuseOutliers; j < k; ++j) {
+            const int c = pa.v_idx[slot + j] & (kHeadDim - 1);
+            const float dv = half_bits_to_float(pa.v_val[slot + j]) - zv * sv;
+            atomicAdd(my_osi + c, static_cast<int>(rintf(pr * dv * sc)));
+          }
+        }
       }
     }
     wave_lds_sync();
@@ -422,7 +421,7 @@ __global__ __launch_bounds__(kFuseThreads) void fused_decode_kernel(QkArgs a, Pv
 #pragma unroll
     for (int w = 0; w < kFuseWaves; ++w) {
       const float f = wml[2 * w] > -INFINITY ? expf(wml[2 * w] - M) : 0.0f;
-      o += f * (wo[w * kHeadDim + c] + osp[w * kHeadDim + c]);
+      o += f * wo[w * kHeadDim + c];
       l += f * wml[2 * w + 1];
     }
     float* dst = pa.partial + ((static_cast<size_t>(seq) * a.n_q_heads + kvh) * pa.n_parts + blockIdx.x) * (kHeadDim + 2);
@@ -441,7 +440,7 @@ hipError_t launch_fused_t(int batch, const QkArgs& a0, const PvArgs& p0, hipStre
   PvArgs pa = p0;
   constexpr int kPairEntries = 1 << (2 * VB);
   const size_t lds = 2 * Sh::kBufBytes + kHeadDim * 4 + 2 * kHalf * 8 + kHalf * 8 + kPairEntries * 4 +
-                     3 * kFuseWaves * kHeadDim * 4 + 2 * kFuseWaves * 4;
+                     2 * kFuseWaves * kHeadDim * 4 + 2 * kFuseWaves * 4;
   static const bool attr_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(&fused_decode_kernel<KB, VB>),
                                                   hipFuncAttributeMaxDynamicSharedMemorySize,
                                                   static_cast<int>(lds)) == hipSuccess;

@@ -12,7 +12,8 @@
 // (max, sum) softmax state and the next tile's data already in flight.  Per tile:
 //   * lane = token: the wave's max logit per query head rescales the running state,
 //     p_t = exp(l_t - m), w_t = p_t * s_t, and the outlier corrections
-//     p_t * (x_c - zc * s_t) are added into the wave's own LDS row of channels;
+//     p_t * (x_c - zc * s_t) are summed per channel in fixed point (integer atomics on
+//     the wave's own LDS rows, so the sums do not depend on the order the atomics land);
 //   * lane = channel pair (2l, 2l+1): the 2b-bit field holding two consecutive tokens of
 //     one channel indexes a small table of fp16 pairs (cb[a], cb[b]).  With one query head
 //     w_t reaches every lane as a scalar operand (read from lane t) of a packed fp16 dot
@@ -60,7 +61,6 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
   __shared__ uint32_t lut2[kPairEntries];         // fp16 (cb[a], cb[b]) for a token pair
   __shared__ uint2 lut4[kQuadEntries];            // fp16 (cb[a], cb[b], cb[c], cb[d]) for a token quad
   __shared__ uint32_t cbs[kNc];                   // fp16 codebook (for building lut4)
-  __shared__ float osp[kWaves][G][kHeadDim];      // per-wave outlier corrections past the first two
   __shared__ int osi[kWaves][G][kHeadDim];        // per-wave, per-tile fixed-point outlier sums
   __shared__ float wm[kWaves][G], wl[kWaves][G];  // per-wave max and sum
   __shared__ float wo[kWaves][G][kHeadDim];       // per-wave weighted sums
@@ -165,10 +165,7 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
 
   lut2[tid & (kPairEntries - 1)] = cb_a | (cb_b << 16);  // threads sharing an entry write the same value
   if (kQuad && tid < kNc) cbs[tid] = cb_a;               // cb_a = cb[tid] for tid < 2^VB
-  for (int e = tid; e < kWaves * G * kHeadDim; e += kThreads) {
-    (&osp[0][0][0])[e] = 0.0f;
-    (&osi[0][0][0])[e] = 0;
-  }
+  for (int e = tid; e < kWaves * G * kHeadDim; e += kThreads) (&osi[0][0][0])[e] = 0;
   if constexpr (kMfma) {
     for (int e = tid; e < kWaves * 4 * kGroups * kTile; e += kThreads) (&wsh[0][0][0])[e] = static_cast<_Float16>(0.0f);
   }
@@ -191,7 +188,6 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
     lsum[h] = 0.0f;
     acc[h][0] = acc[h][1] = 0.0f;
   }
-  float* my_osp = &osp[wave][0][0];
 
   auto compute = [&](int tile, const TileData<VB, G>& d) {
     const int t = tile * kTile + lane;
@@ -208,8 +204,6 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
         acc[h][0] *= sc;
         acc[h][1] *= sc;
         lsum[h] *= sc;
-        my_osp[h * kHeadDim + 2 * lane] *= sc;
-        my_osp[h * kHeadDim + 2 * lane + 1] *= sc;
       }
       pr[h] = valid ? __expf(lg - m_run[h]) : 0.0f;  // hardware exp2 of x log2(e): relative error < 4e-6 for x >= -100
       lsum[h] += pr[h];
@@ -217,21 +211,31 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
     }
     wave_lds_sync();
     // Outliers: the dense code at an outlier channel is the zero code, so channel c gets
-    // p_t * (x_c - zc * s_t).  Float atomics on LDS are slow on this device (about 190
-    // cycles per wave instruction), so the first two outliers of every token are summed
-    // per tile in 32-bit fixed point with integer atomics: the scale 2^(23 - e), with
-    // 2^e above the tile's largest |contribution|, keeps each term below 2^23 and the sum
-    // of at most 128 terms inside int32, rounding each term to 2^-23 of that maximum.
-    // Each channel lane folds its two channels into its accumulators after the dense part.
+    // p_t * (x_c - zc * s_t).  These are summed per tile in 32-bit fixed point with integer
+    // LDS atomics (float atomics on LDS are slow on this device, about 190 cycles per wave
+    // instruction, and their sums would depend on the order they land): the scale
+    // 2^(23 - e), with 2^e above the tile's largest |contribution| over every outlier and
+    // head, keeps each term below 2^23, and a channel receives at most one term per token
+    // (a vector's outlier channels are distinct), so a tile's sum stays below 2^29.  Each
+    // term is rounded to 2^-24 of 2^e.  The first two outliers of every token travel with
+    // the tile data; further ones are read twice from global memory (cache hits the second
+    // time), once for the scale and once for the sums.  Each channel lane folds its two
+    // channels into its accumulators after the atomics.
     float unscale = 0.0f;
     bool have_fixed = false;
     {
       const float dv0 = half_bits_to_float(d.ov[0]) - zc * s;
       const float dv1 = half_bits_to_float(d.ov[1]) - zc * s;
       const int c0 = d.oi[0] & (kHeadDim - 1), c1 = d.oi[1] & (kHeadDim - 1);  // stale bytes past the length
+      const bool more = k > kPrefetchOutliers && valid;
+      const size_t slot = (stream * S + t) * k;
+      float dmax = fmaxf(kp >= 1 ? fabsf(dv0) : 0.0f, kp >= 2 ? fabsf(dv1) : 0.0f);
+      if (more) {
+        for (int j = kPrefetchOutliers; j < k; ++j) dmax = fmaxf(dmax, fabsf(half_bits_to_float(a.v_val[slot + j]) - zc * s));
+      }
       float mloc = 0.0f;
 #pragma unroll
-      for (int h = 0; h < G; ++h) mloc = fmaxf(mloc, pr[h] * fmaxf(kp >= 1 ? fabsf(dv0) : 0.0f, kp >= 2 ? fabsf(dv1) : 0.0f));
+      for (int h = 0; h < G; ++h) mloc = fmaxf(mloc, pr[h] * dmax);
       const float m = wave_max_f32(mloc);  // one scale for every head of the group
       have_fixed = m > 0.0f;               // wave-uniform
       if (have_fixed) {
@@ -244,15 +248,14 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
           if (kp >= 1) atomicAdd(row + c0, static_cast<int>(rintf(pr[h] * dv0 * sc)));
           if (kp >= 2) atomicAdd(row + c1, static_cast<int>(rintf(pr[h] * dv1 * sc)));
         }
-      }
-    }
-    if (k > kPrefetchOutliers && valid) {
-      const size_t slot = stream * S + t;
-      for (int j = kPrefetchOutliers; j < k; ++j) {
-        const int c = a.v_idx[slot * k + j] & (kHeadDim - 1);
-        const float dv = half_bits_to_float(a.v_val[slot * k + j]) - zc * s;
+        if (more) {
+          for (int j = kPrefetchOutliers; j < k; ++j) {
+            const int c = a.v_idx[slot + j] & (kHeadDim - 1);
+            const float dv = half_bits_to_float(a.v_val[slot + j]) - zc * s;
 #pragma unroll
-        for (int h = 0; h < G; ++h) atomicAdd(&my_osp[h * kHeadDim + c], pr[h] * dv);
+            for (int h = 0; h < G; ++h) atomicAdd(&osi[wave][h][c], static_cast<int>(rintf(pr[h] * dv * sc)));
+          }
+        }
       }
     }
     wave_lds_sync();
@@ -422,7 +425,7 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const float f = wm[w][h] > -INFINITY ? expf(wm[w][h] - M) : 0.0f;
-      o += f * (wo[w][h][c] + osp[w][h][c]);
+      o += f * wo[w][h][c];
       l += f * wl[w][h];
     }
     float* dst = part_ptr(h);
