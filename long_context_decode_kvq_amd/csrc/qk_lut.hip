@@ -42,6 +42,8 @@ constexpr int kLutThreads = 64 * kLutWaves;
 constexpr int kLutSuper = kLutWaves * kTile; // tokens per super-tile
 constexpr int kLutPrefetchOutliers = 2;      // outliers per token fetched with the record
 constexpr int kLutAhead = 7;                 // table reads in flight ahead of the FMAs (at most 15)
+constexpr int kLutRows = kHalf / kLutWaves;  // table rows (rotary pairs) each wave fills
+static_assert(kLutRows >= 4 && kLutRows <= 16, "a wave's rows are broadcast from lanes 0..15 of a DPP row");
 
 template <int KB>
 struct LutShape {
@@ -142,11 +144,12 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
 
   // ---- set-up inputs, then the first two records ---------------------------------------
   // Thread i < 64 stages rotary pair i's query, key scales and frequency in LDS.  Lane l of
-  // wave w distributes the build coefficients of one of the eight pairs w + 8 m whose rows
-  // the wave fills, placed for the DPP row broadcasts of the build: 3-bit rows, m = l & 7
-  // (lane m of every 16-lane row holds pair w + 8 m); 2-bit rows, lane 16 r + f holds
-  // m = 4 f + r (fill step f finds its row's pair at lane f of the row).
-  const int P = KB == 3 ? wave + kLutWaves * (lane & 7) : wave + kLutWaves * ((lane >> 4) + 4 * (lane & 1));
+  // wave w distributes the build coefficients of one of the kLutRows pairs w + W m (W waves)
+  // whose rows the wave fills, placed for the DPP row broadcasts of the build: 3-bit rows,
+  // m = l mod kLutRows (lane m of every 16-lane row holds pair w + W m); 2-bit rows, lane
+  // 16 r + f holds m = 4 f + r (fill step f finds its row's pair at lane f of the row).
+  const int P = KB == 3 ? wave + kLutWaves * (lane & (kLutRows - 1))
+                        : wave + kLutWaves * ((lane >> 4) + 4 * (lane & (kLutRows / 4 - 1)));
   const int ip = tid & (kHalf - 1);
   const size_t qbase = (static_cast<size_t>(seq) * a.n_q_heads + kvh) * kHeadDim;
   uint32_t qraw[2];
@@ -213,10 +216,10 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
     constexpr int B = decltype(bc)::value;
     float2* T = lut + B * (Sh::kBufBytes / 8);
     if constexpr (KB == 3) {
-      // wave w fills the rows of pairs w + 8 m, m < 8; lane m of every 16-lane row holds
-      // their coefficients and hands them over by DPP row broadcast inside the multiplies
+      // wave w fills the rows of pairs w + W m, m < kLutRows; lane m of every 16-lane row
+      // holds their coefficients and hands them over by DPP row broadcast inside the multiplies
       asm volatile("s_nop 1" : "+v"(cc.x), "+v"(cc.y), "+v"(cc.z), "+v"(cc.w));  // DPP read wait states
-      static_for<0, 8>([&](auto mc) {
+      static_for<0, kLutRows>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         T[(wave + kLutWaves * m) * kNe + lane] = lut_entry_bcast<m>(cc.x, cc.y, cc.z, cc.w, cba, cbb);
       });
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
       // 16 entries per row: fill step f covers the rows of 4 pairs, m = 4 f + (lane >> 4),
       // whose coefficients lane f of each 16-lane row holds (DPP row broadcast).
       asm volatile("s_nop 1" : "+v"(cc.x), "+v"(cc.y), "+v"(cc.z), "+v"(cc.w));  // DPP read wait states
-      static_for<0, 2>([&](auto fc) {
+      static_for<0, kLutRows / 4>([&](auto fc) {
         constexpr int f = decltype(fc)::value;
         const int i = wave + kLutWaves * (4 * f + (lane >> 4));
         T[i * kNe + (lane & 15)] = lut_entry_bcast<f>(cc.x, cc.y, cc.z, cc.w, cba, cbb);
