@@ -32,9 +32,16 @@
  *   v_codes   uint8 [B][H][S/64][D*8*v_bits]   channel-major 64-token tiles: inside a
  *             tile, channel c owns bytes [c*8*b, (c+1)*8*b): its 64 codes in token order
  *             as a little-endian bitstream.
- *   k_out_idx uint8  [B][H][S][k]  outlier channels of each key vector, ascending
+ *   k_out_idx uint8  [B][H][S][k]  outlier channels of each key vector, strictly
+ *                                  ascending (under the per-channel key rule, unused
+ *                                  slots after them hold channel 255)
  *   k_out_val uint16 [B][H][S][k]  their fp16 values, unchanged
- *   v_out_idx, v_out_val           the same for values
+ *   v_out_idx, v_out_val           the same for values: always k distinct channels,
+ *                                  strictly ascending.  The value pass sums a tile's
+ *                                  outlier terms in 32-bit fixed point and relies on
+ *                                  this (at most one term per channel and token); a
+ *                                  cache with repeated value channels is outside the
+ *                                  contract (its outputs are undefined, nothing faults)
  *   v_scale   uint16 [B][H][S]     fp16 per-vector value scale (max |dense entry|)
  *   k_scale   float  [H][D]        frozen per-channel key scale (caller calibrated)
  *   k_codebook, v_codebook  fp16 [2^bits] (uint16_t bits), strictly ascending, in [-1, 1];
