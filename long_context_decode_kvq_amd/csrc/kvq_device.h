@@ -115,6 +115,65 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return lane_f32(r, 63);
 }
 #undef KVQ_WAVE_MAX_STEPS
+// Two or four independent float wave maxima in one pass, the same six DPP steps with the
+// chains interleaved: with four, each DPP read follows the write of its source by three
+// other instructions; with two, by one instruction and an s_nop 0.  One s_nop 1 covers the
+// inputs' writes before the block.
+#define KVQ_MAX_DPP(D, S, CTL) "v_max_f32_dpp %" #D ", %" #S ", %" #S " " CTL "\n\t"
+#define KVQ_CTL1 "quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+#define KVQ_CTL2 "quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+#define KVQ_CTL3 "row_half_mirror row_mask:0xf bank_mask:0xf"
+#define KVQ_CTL4 "row_mirror row_mask:0xf bank_mask:0xf"
+#define KVQ_CTL5 "row_bcast:15 row_mask:0xa bank_mask:0xf"
+#define KVQ_CTL6 "row_bcast:31 row_mask:0xc bank_mask:0xf"
+#define KVQ_MAX2_STEP(CTL) "s_nop 0\n\t" KVQ_MAX_DPP(0, 0, CTL) KVQ_MAX_DPP(1, 1, CTL)
+#define KVQ_MAX4_STEP(CTL) KVQ_MAX_DPP(0, 0, CTL) KVQ_MAX_DPP(1, 1, CTL) KVQ_MAX_DPP(2, 2, CTL) KVQ_MAX_DPP(3, 3, CTL)
+__device__ __forceinline__ void wave_max2_f32(float a, float b, float& ma, float& mb) {
+  float r0, r1;
+  asm("s_nop 1\n\t" KVQ_MAX_DPP(0, 2, KVQ_CTL1) KVQ_MAX_DPP(1, 3, KVQ_CTL1)
+      KVQ_MAX2_STEP(KVQ_CTL2) KVQ_MAX2_STEP(KVQ_CTL3) KVQ_MAX2_STEP(KVQ_CTL4) KVQ_MAX2_STEP(KVQ_CTL5)
+      KVQ_MAX2_STEP(KVQ_CTL6)
+      : "=&v"(r0), "=&v"(r1)
+      : "v"(a), "v"(b));
+  ma = lane_f32(r0, 63);
+  mb = lane_f32(r1, 63);
+}
+__device__ __forceinline__ void wave_max4_f32(const float (&v)[4], float (&m)[4]) {
+  float r0, r1, r2, r3;
+  asm("s_nop 1\n\t" KVQ_MAX_DPP(0, 4, KVQ_CTL1) KVQ_MAX_DPP(1, 5, KVQ_CTL1) KVQ_MAX_DPP(2, 6, KVQ_CTL1)
+      KVQ_MAX_DPP(3, 7, KVQ_CTL1) KVQ_MAX4_STEP(KVQ_CTL2) KVQ_MAX4_STEP(KVQ_CTL3) KVQ_MAX4_STEP(KVQ_CTL4)
+      KVQ_MAX4_STEP(KVQ_CTL5) KVQ_MAX4_STEP(KVQ_CTL6)
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+  m[0] = lane_f32(r0, 63);
+  m[1] = lane_f32(r1, 63);
+  m[2] = lane_f32(r2, 63);
+  m[3] = lane_f32(r3, 63);
+}
+// G wave maxima (G = 1, 2, 4, 8), in as few interleaved passes as that allows.
+template <int G>
+__device__ __forceinline__ void wave_max_n_f32(const float (&v)[G], float (&m)[G]) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "one, two, four or eight maxima");
+  if constexpr (G == 1) {
+    m[0] = wave_max_f32(v[0]);
+  } else if constexpr (G == 2) {
+    wave_max2_f32(v[0], v[1], m[0], m[1]);
+  } else if constexpr (G == 4) {
+    wave_max4_f32(v, m);
+  } else {
+    wave_max4_f32(*reinterpret_cast<const float(*)[4]>(&v[0]), *reinterpret_cast<float(*)[4]>(&m[0]));
+    wave_max4_f32(*reinterpret_cast<const float(*)[4]>(&v[4]), *reinterpret_cast<float(*)[4]>(&m[4]));
+  }
+}
+#undef KVQ_MAX4_STEP
+#undef KVQ_MAX2_STEP
+#undef KVQ_CTL1
+#undef KVQ_CTL2
+#undef KVQ_CTL3
+#undef KVQ_CTL4
+#undef KVQ_CTL5
+#undef KVQ_CTL6
+#undef KVQ_MAX_DPP
 __device__ __forceinline__ float wave_sum_f32(float v) {
   v += dpp_f32<0xB1>(v);
   v += dpp_f32<0x4E>(v);

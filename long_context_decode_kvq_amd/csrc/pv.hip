@@ -193,11 +193,14 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
     const int t = tile * kTile + lane;
     const bool valid = t < L;
     const float s = half_bits_to_float(d.sv);
-    float pr[G], wts[G];
+    float pr[G], wts[G], lgv[G], mtv[G], wmaxv[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) lgv[h] = valid ? d.lg[h] : -INFINITY;
+    wave_max_n_f32<G>(lgv, mtv);  // the tile's max logit of every head, in one pass
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float lg = valid ? d.lg[h] : -INFINITY;
-      const float mt = wave_max_f32(lg);
+      const float lg = lgv[h];
+      const float mt = mtv[h];
       if (mt > m_run[h]) {  // wave-uniform: rescale the running state to the new max
         const float sc = m_run[h] > -INFINITY ? expf(m_run[h] - mt) : 0.0f;
         m_run[h] = mt;
@@ -236,7 +239,15 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
       float mloc = 0.0f;
 #pragma unroll
       for (int h = 0; h < G; ++h) mloc = fmaxf(mloc, pr[h] * dmax);
-      const float m = wave_max_f32(mloc);  // one scale for every head of the group
+      // one outlier scale for every head of the group; with it, the tile's largest weight of
+      // every head (the dense part's prescale)
+      float m;
+      if constexpr (G == 1) {
+        wave_max2_f32(wts[0], mloc, wmaxv[0], m);
+      } else {
+        wave_max_n_f32<G>(wts, wmaxv);
+        m = wave_max_f32(mloc);
+      }
       have_fixed = m > 0.0f;               // wave-uniform
       if (have_fixed) {
         const int e = min(max(static_cast<int>((__builtin_bit_cast(uint32_t, m) >> 23) & 0xffu) - 126, -100), 100);
@@ -287,7 +298,7 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
       _Float16* wrow = &wsh[kMfma ? wave : 0][0][0];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float wmax = wave_max_f32(wts[h]);
+        const float wmax = wmaxv[h];
         const int ex = wmax > 0.0f ? static_cast<int>((__builtin_bit_cast(uint32_t, wmax) >> 23) & 0xffu) - 127 : 0;
         const int sh = min(max(13 - ex, -100), 100);  // 2^sh * wmax in [2^13, 2^14)
         unsc[h] = __builtin_bit_cast(float, static_cast<uint32_t>(127 - sh) << 23);
@@ -332,7 +343,7 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
       uint32_t wpair[G];
   #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float wmax = wave_max_f32(wts[h]);
+        const float wmax = wmaxv[h];
         const int ex = wmax > 0.0f ? static_cast<int>((__builtin_bit_cast(uint32_t, wmax) >> 23) & 0xffu) - 127 : 0;
         const int sh = min(max(13 - ex, -100), 100);  // 2^sh * wmax in [2^13, 2^14)
         unsc[h] = __builtin_bit_cast(float, static_cast<uint32_t>(127 - sh) << 23);
