@@ -309,24 +309,35 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
       pv_float4 dacc[kGroups][2];
 #pragma unroll
       for (int g = 0; g < kGroups; ++g) dacc[g][0] = dacc[g][1] = pv_float4{0.0f, 0.0f, 0.0f, 0.0f};
-      static_for<0, kTile / 4>([&](auto jc) {
+      // The operands of step j + 1 (table lookups and weight rows) are requested before the
+      // products of step j, so the wait before each step's products leaves the next step's
+      // reads in flight instead of draining every LDS read (they complete in order).
+      uint2 bq[2][2], aw[2][kGroups];
+      auto fetch = [&](auto jc) __attribute__((always_inline)) {
         constexpr int j = decltype(jc)::value;
-        uint2 bq[2];
+        constexpr int b = j & 1;
         if constexpr (kQuad) {
-          bq[0] = lut4[field<4 * VB, 4 * VB * j>(d.w)];
-          bq[1] = lut4[field<4 * VB, kChanBits + 4 * VB * j>(d.w)];
+          bq[b][0] = lut4[field<4 * VB, 4 * VB * j>(d.w)];
+          bq[b][1] = lut4[field<4 * VB, kChanBits + 4 * VB * j>(d.w)];
         } else {
-          bq[0] = make_uint2(lut2[field<2 * VB, 4 * VB * j>(d.w)], lut2[field<2 * VB, 4 * VB * j + 2 * VB>(d.w)]);
-          bq[1] = make_uint2(lut2[field<2 * VB, kChanBits + 4 * VB * j>(d.w)],
-                             lut2[field<2 * VB, kChanBits + 4 * VB * j + 2 * VB>(d.w)]);
+          bq[b][0] = make_uint2(lut2[field<2 * VB, 4 * VB * j>(d.w)], lut2[field<2 * VB, 4 * VB * j + 2 * VB>(d.w)]);
+          bq[b][1] = make_uint2(lut2[field<2 * VB, kChanBits + 4 * VB * j>(d.w)],
+                                lut2[field<2 * VB, kChanBits + 4 * VB * j + 2 * VB>(d.w)]);
         }
 #pragma unroll
+        for (int g = 0; g < kGroups; ++g) aw[b][g] = *reinterpret_cast<const uint2*>(wa + g * (4 * kTile * 2) + j * 8);
+      };
+      fetch(std::integral_constant<int, 0>{});
+      static_for<0, kTile / 4>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        constexpr int b = j & 1;
+        if constexpr (j + 1 < kTile / 4) fetch(std::integral_constant<int, j + 1>{});
+#pragma unroll
         for (int g = 0; g < kGroups; ++g) {
-          const uint2 aw = *reinterpret_cast<const uint2*>(wa + g * (4 * kTile * 2) + j * 8);
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            dacc[g][hf] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(pv_half4, aw), __builtin_bit_cast(pv_half4, bq[hf]),
-                                                             dacc[g][hf], 0, 0, 0);
+            dacc[g][hf] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(pv_half4, aw[b][g]),
+                                                             __builtin_bit_cast(pv_half4, bq[b][hf]), dacc[g][hf], 0, 0, 0);
             asm volatile("" : "+a"(dacc[g][hf]));  // keeps each product next to its operands
           }
         }

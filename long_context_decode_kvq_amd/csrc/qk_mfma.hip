@@ -350,6 +350,16 @@ __global__ __launch_bounds__(kMfThreads) void qk_mfma_kernel(QkArgs a) {
       va[i % (kMfAhead + 1)] = v.x;
       vb[i % (kMfAhead + 1)] = v.y;
     };
+    // With one A operand per step (g <= 4, fp16 queries) the query row of MFMA step j + 1 is
+    // requested right after the products of step j: read just before its own product, its
+    // wait would also drain the table reads issued ahead (LDS reads complete in order).  With
+    // two or four per step the extra live registers cost spills, and each row is read just
+    // before its product.
+    constexpr bool kEarlyA = kGroups * kParts == 1;
+    auto a_row = [&](int gp, int j) __attribute__((always_inline)) {
+      return *reinterpret_cast<const uint2*>(qa_lane + (gp * 4 * Sh::kSteps + j) * 8);
+    };
+    uint2 aw_next = kEarlyA ? a_row(0, 0) : make_uint2(0u, 0u);
     static_for<0, kMfAhead>([&](auto ic) { issue(ic); });
     uint32_t hp[2];
     static_for<0, kHalf>([&](auto ic) {
@@ -366,12 +376,13 @@ __global__ __launch_bounds__(kMfThreads) void qk_mfma_kernel(QkArgs a) {
         for (int g = 0; g < kGroups; ++g)
 #pragma unroll
           for (int part = 0; part < kParts; ++part) {
-            const uint2 aw = *reinterpret_cast<const uint2*>(qa_lane + ((g * kParts + part) * 4 * Sh::kSteps + j) * 8);
+            const uint2 aw = kEarlyA ? aw_next : a_row(g * kParts + part, j);
             acc[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(mf_half4, aw), bop, acc[g], 0, 0, 0);
             // keeps the product here, so that the rotated pairs die at once instead of the
             // compiler sinking every MFMA to the end of the loop
             asm volatile("" : "+v"(acc[g]));
           }
+        if constexpr (kEarlyA && j + 1 < Sh::kSteps) aw_next = a_row(0, j + 1);
       }
       if constexpr ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     });
