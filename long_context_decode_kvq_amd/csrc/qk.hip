@@ -312,19 +312,34 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
 #pragma unroll
       for (int u = 0; u < kPartials; ++u) accp[h][u] = 0.0f;
 
-    static_for<0, kHalf>([&](auto ic) {
+    // One head: the pair's table entry and R(tau) are requested kAhead pairs before their
+    // arithmetic (a rolling window of registers), so each wait leaves the later reads in
+    // flight; read just before use, every pair's wait drained all LDS reads (they complete
+    // in order).  Grouped heads also read their query pairs from LDS per pair and keep the
+    // reads beside their use.
+    constexpr int kAhead = kFoldScale ? 6 : 0;
+    uint32_t e2w[kAhead + 1];
+    float crw[kAhead + 1], ciw[kAhead + 1];
+    auto fetch = [&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      const uint32_t e2 = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(lutp) +
-                                                             Tab::at(field<2 * KB, 2 * KB * i>(d.w), tab_base));
-      float cr, ci;
+      constexpr int r = i % (kAhead + 1);
+      e2w[r] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(lutp) +
+                                                  Tab::at(field<2 * KB, 2 * KB * i>(d.w), tab_base));
       if constexpr (i < kRegPairs) {
-        cr = er[i];
-        ci = ei[i];
+        crw[r] = er[i];
+        ciw[r] = ei[i];
       } else {
         const float2 e = et[i][lane];
-        cr = e.x;
-        ci = e.y;
+        crw[r] = e.x;
+        ciw[r] = e.y;
       }
+    };
+    static_for<0, kAhead>([&](auto ic) { fetch(ic); });
+    static_for<0, kHalf>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + kAhead < kHalf) fetch(std::integral_constant<int, i + kAhead>{});
+      const uint32_t e2 = e2w[i % (kAhead + 1)];
+      const float cr = crw[i % (kAhead + 1)], ci = ciw[i % (kAhead + 1)];
       if constexpr (kFoldScale) {
         accp[0][i % kPartials] =
             pair_term<i % 16>(accp[0][i % kPartials], e2, cr, ci, alp[i / 16], bet[i / 16], gam[i / 16], ndl[i / 16]);
@@ -340,6 +355,7 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
           accp[h][i % kPartials] = fmaf(qq.y, yb, fmaf(qq.x, ya, accp[h][i % kPartials]));
         }
       }
+      if constexpr (kAhead > 0 && (i & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // keeps the reads ahead
     });
 
     float acc[G];
