@@ -236,27 +236,34 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   };
 
   // Outlier slot operands, requested from LDS before the pair loop.
+  // Only the reads happen here; the arithmetic on them waits for out_term, after the pair
+  // loop (used at once, the channel's scale would make the step wait for every LDS read).
   struct OutOps {
-    float dv;      // stored value minus the decoded zero code (0 for an unused slot)
-    float2 th;     // theta/2pi of its pair (hi, lo)
-    float2 p;      // rotated query pair of its pair
-    bool lo_half;  // channel < 64
+    uint32_t vbits;  // the stored fp16 value
+    float sc;        // its channel's key scale
+    bool used;       // false for an unused slot (per-channel rule): adds nothing
+    float2 th;       // theta/2pi of its pair (hi, lo)
+    float2 p;        // rotated query pair of its pair
+    bool lo_half;    // channel < 64
   };
   auto out_ops = [&](uint32_t c, uint32_t vbits, const float2* pab) __attribute__((always_inline)) {
     OutOps o;
-    const bool used = c != kNoOutlier;  // an unused slot (per-channel rule) adds nothing
-    c &= kHeadDim - 1;                  // a token past the length may hold stale bytes
+    o.used = c != kNoOutlier;
+    c &= kHeadDim - 1;  // a token past the length may hold stale bytes
     const int i = c & (kHalf - 1);
-    o.dv = used ? half_bits_to_float(vbits) - zc * ks[c] : 0.0f;
+    o.vbits = vbits;
+    o.sc = ks[c];
     o.th = thl[i];
     o.p = pab[i];
     o.lo_half = c < kHalf;
     return o;
   };
   auto out_term = [&](const OutOps& o) __attribute__((always_inline)) {
+    // stored value minus the decoded zero code, at the channel's rotated query coefficient
+    const float dv = o.used ? half_bits_to_float(o.vbits) - zc * o.sc : 0.0f;
     const float ph = fmaf(tauf, o.th.y, __builtin_amdgcn_fractf(tauf * o.th.x));
     const float cs = __builtin_amdgcn_cosf(ph), sn = __builtin_amdgcn_sinf(ph);
-    return o.dv * (o.lo_half ? (o.p.x * cs + o.p.y * sn) : (o.p.y * cs - o.p.x * sn));
+    return dv * (o.lo_half ? (o.p.x * cs + o.p.y * sn) : (o.p.y * cs - o.p.x * sn));
   };
 
   // ---- one tile of super-tile s from table buffer B, and the rows of s + 1 -------------
