@@ -290,31 +290,35 @@ __global__ __launch_bounds__(kMfThreads) void qk_mfma_kernel(QkArgs a) {
     }
   };
 
-  // Outlier slot operands, requested from LDS before the pair loop.
+  // Outlier slot operands, requested from LDS before the pair loop; the arithmetic on them
+  // waits for out_add, after it (used at once, the channel's scale would make the step wait
+  // for every LDS read in flight).
   struct OutOps {
-    float dv;      // stored value minus the decoded zero code (0 for an unused slot)
-    float2 th;     // theta/2pi of its pair (hi, lo)
-    int i;         // its pair
-    bool lo_half;  // channel < 64
+    uint32_t vbits;  // the stored fp16 value; above 0xffff for an unused slot (per-channel rule)
+    float sc;        // its channel's key scale
+    float2 th;       // theta/2pi of its pair (hi, lo)
+    int i;           // its pair
+    bool lo_half;    // channel < 64
   };
   // Channel c of pair i rotated by tau theta_i meets the rotated query pair (p_a, p_b) as
   // p_a cos + p_b sin (c = i) or p_b cos - p_a sin (c = i + 64): both are p_a u + p_b v
   // with (u, v) chosen once per outlier and scaled by its value, two FMAs per head.
   auto out_ops = [&](uint32_t c, uint32_t vbits) __attribute__((always_inline)) {
     OutOps o;
-    const bool used = c != kNoOutlier;  // an unused slot (per-channel rule) adds nothing
-    c &= kHeadDim - 1;                  // a token past the length may hold stale bytes
+    o.vbits = c != kNoOutlier ? vbits : 0xffffffffu;  // an unused slot adds nothing
+    c &= kHeadDim - 1;                                // a token past the length may hold stale bytes
     o.i = c & (kHalf - 1);
-    o.dv = used ? half_bits_to_float(vbits) - zc * ks[c] : 0.0f;
+    o.sc = ks[c];
     o.th = thl[o.i];
     o.lo_half = c < kHalf;
     return o;
   };
   auto out_add = [&](const OutOps& o, const float2* pab, float (&ol)[G]) __attribute__((always_inline)) {
+    const float dv = o.vbits <= 0xffffu ? half_bits_to_float(o.vbits) - zc * o.sc : 0.0f;  // minus the decoded zero code
     const float ph = fmaf(tauf, o.th.y, __builtin_amdgcn_fractf(tauf * o.th.x));
     const float cs = __builtin_amdgcn_cosf(ph), sn = __builtin_amdgcn_sinf(ph);
-    const float u = o.dv * (o.lo_half ? cs : -sn);
-    const float v = o.dv * (o.lo_half ? sn : cs);
+    const float u = dv * (o.lo_half ? cs : -sn);
+    const float v = dv * (o.lo_half ? sn : cs);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float2 p = pab[h * kHalf + o.i];
