@@ -11,8 +11,8 @@
 //   * R(-t0), folded into the query once per tile (lane i handles rotary pair i; the
 //     tile-base phase is formed once per wave from a float64 angle and then advanced by
 //     the fixed step 64 * theta_i), and
-//   * R(tau), tau = lane < 64, from a per-block table (the first kRegPairs pairs
-//     copied into registers, the rest read from LDS).
+//   * R(tau), tau = lane < 64, from a per-block LDS table (with all 64 pairs in registers
+//     the kernel would drop to two waves per SIMD; 16 or 32 of them measured no faster).
 // The record keeps the two halves of rotary pair i side by side, so one 2b-bit field
 // indexes a small shared table of fp16 pairs (cb[a], cb[b]); the fp16 values feed
 // mixed-precision FMAs directly (exact conversion).  With one query head per kv head the
@@ -30,10 +30,6 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
-
-#ifndef KVQ_QK_REG_PAIRS
-#define KVQ_QK_REG_PAIRS 0
-#endif
 
 namespace kvq {
 namespace {
@@ -70,8 +66,6 @@ struct Rec {
   uint32_t oi[2], ov[2];  // its first two outliers: channels and fp16 value bits
 };
 constexpr int kPartials = 4;  // partial sums per logit
-constexpr int kRegPairsDefault = KVQ_QK_REG_PAIRS;
-static_assert(kRegPairsDefault >= 0 && kRegPairsDefault <= kHalf, "register pairs out of range");
 
 template <int KB, int G>
 __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
@@ -79,8 +73,6 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   constexpr int kPairEntries = 1 << (2 * KB);
   static_assert(KB == 4, "4-bit keys (2/3-bit keys use the table kernels)");
   constexpr bool kFoldScale = G == 1;
-  // R(tau) of the first kRegPairs pairs is held in registers, the rest read from LDS
-  constexpr int kRegPairs = kRegPairsDefault;
 
   __shared__ float2 et[kHalf][kTile];       // R(tau) for pair i: (cos, sin) of tau * theta_i
   using Tab = RepTable<kPairEntries>;
@@ -249,14 +241,6 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
     ss[j] = st.y;
   }
 
-  // R(tau) for this lane's token: the first kRegPairs pairs in registers.
-  float er[kRegPairs > 0 ? kRegPairs : 1], ei[kRegPairs > 0 ? kRegPairs : 1];
-#pragma unroll
-  for (int i = 0; i < kRegPairs; ++i) {
-    const float2 e = et[i][lane];
-    er[i] = e.x;
-    ei[i] = e.y;
-  }
   if (n_tiles <= 0) return;  // after the block's last barrier
 
   const int my_slot = lane >> 4;
@@ -325,14 +309,9 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
       constexpr int r = i % (kAhead + 1);
       e2w[r] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(lutp) +
                                                   Tab::at(field<2 * KB, 2 * KB * i>(d.w), tab_base));
-      if constexpr (i < kRegPairs) {
-        crw[r] = er[i];
-        ciw[r] = ei[i];
-      } else {
-        const float2 e = et[i][lane];
-        crw[r] = e.x;
-        ciw[r] = e.y;
-      }
+      const float2 e = et[i][lane];  // R(tau) of pair i for this lane's token
+      crw[r] = e.x;
+      ciw[r] = e.y;
     };
     static_for<0, kAhead>([&](auto ic) { fetch(ic); });
     static_for<0, kHalf>([&](auto ic) {
