@@ -51,6 +51,12 @@ CASES = {
     "mha2_2bit_k3": (_wl("llama7b_1m_2bit", n_q_heads=2, n_kv_heads=2, seq_len=1100, outlier_frac=0.02), [1100], None),
     "gqa4_k5_ragged": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=4, n_kv_heads=1, seq_len=900, outlier_frac=0.035),
                        [900, 333], None),
+    # 4-bit keys and values with k = 5: the 4-bit key kernel's loop over the outliers past
+    # the second, with one head and with grouped heads
+    "mha2_4bit_k5": (_wl("llama7b_128k_4bit", n_q_heads=2, n_kv_heads=2, seq_len=1100, outlier_frac=0.035),
+                     [1100], None),
+    "gqa2_4bit_k5": (_wl("llama7b_128k_4bit", batch=2, n_q_heads=4, n_kv_heads=2, seq_len=700, outlier_frac=0.035),
+                     [700, 131], None),
     # grouped heads with 2-bit keys (the per-pair table path of the general kernel)
     "gqa2_2bit": (_wl("llama3_8b_gqa_b16_64k", batch=2, n_q_heads=4, n_kv_heads=2, seq_len=800, k_bits=2),
                   [800, 391], None),
