@@ -348,12 +348,11 @@ __global__ __launch_bounds__(kFuseThreads) void fused_decode_kernel(QkArgs a, Pv
       }
     }
     wave_lds_sync();
-    if (have_fixed) {  // this tile's fixed-point sums of channels (2l, 2l+1), then clear them
-      int2* cell = reinterpret_cast<int2*>(my_osi + 2 * lane);
-      const int2 q = *cell;
-      acc0 = fmaf(static_cast<float>(q.x), unscale, acc0);
-      acc1 = fmaf(static_cast<float>(q.y), unscale, acc1);
-      *cell = make_int2(0, 0);
+    if (have_fixed) {  // this tile's fixed-point sums of channels (2l, 2l+1), read and cleared by one LDS exchange
+      unsigned long long* cell = reinterpret_cast<unsigned long long*>(my_osi + 2 * lane);
+      const unsigned long long q = __hip_atomic_exchange(cell, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+      acc0 = fmaf(static_cast<float>(static_cast<int>(static_cast<uint32_t>(q))), unscale, acc0);
+      acc1 = fmaf(static_cast<float>(static_cast<int>(static_cast<uint32_t>(q >> 32))), unscale, acc1);
     }
     // Dense part: fp16 weight pairs (w_t, w_t+1) as one scalar operand per two tokens of a
     // packed dot product with the codebook pair; the weights scaled by the power of two
