@@ -269,7 +269,6 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   // ---- one tile of super-tile s from table buffer B, and the rows of s + 1 -------------
   auto step = [&](auto bc, int s, const LutRec<KB>& d, LutRec<KB>& ahead) __attribute__((always_inline)) {
     constexpr int B = decltype(bc)::value;
-    load_rec(s + 2, ahead);
     const bool more = s + 1 < s_hi;
     const float4 cc = coef[((s + 1) & 1) * kHalf + P];  // build coefficients of super-tile s + 1
     const float2* pab = cpab + (s % 3) * kHalf;
@@ -293,6 +292,10 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
     static_for<0, kHalf>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       if constexpr (i + kLutAhead < kHalf) issue(std::integral_constant<int, i + kLutAhead>{});
+      // The record loads of super-tile s + 2 go out here rather than at the step start: their
+      // scalar address arithmetic then overlaps the other wave's FMAs on this SIMD instead of
+      // adding to the start of a step that both waves begin together after the barrier.
+      if constexpr (i == 8) load_rec(s + 2, ahead);
       acc[i & 3] = fmaf(er[i], va[i % (kLutAhead + 1)], fmaf(ei[i], vb[i % (kLutAhead + 1)], acc[i & 3]));
       if constexpr ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     });

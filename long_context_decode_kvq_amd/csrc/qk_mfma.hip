@@ -335,7 +335,6 @@ __global__ __launch_bounds__(kMfThreads) void qk_mfma_kernel(QkArgs a) {
   // ---- one tile of super-tile s from table buffer B, and the rows of s + 1 -------------
   auto step = [&](auto bc, int s, const MfRec<KB>& d, MfRec<KB>& ahead) __attribute__((always_inline)) {
     constexpr int B = decltype(bc)::value;
-    load_rec(s + 2, ahead);
     const bool more = s + 1 < s_hi;
     const float4 cc = coef[((s + 1) & 1) * kHalf + P];  // build coefficients of super-tile s + 1
     const float2* pab = cpab + (s % 3) * G * kHalf;
@@ -369,6 +368,9 @@ __global__ __launch_bounds__(kMfThreads) void qk_mfma_kernel(QkArgs a) {
     static_for<0, kHalf>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       if constexpr (i + kMfAhead < kHalf) issue(std::integral_constant<int, i + kMfAhead>{});
+      // the next records' loads and their scalar address arithmetic, issued inside the loop so
+      // that they overlap the other wave's arithmetic rather than lengthen the step's start
+      if constexpr (i == 8) load_rec(s + 2, ahead);
       const float xa = va[i % (kMfAhead + 1)], xb = vb[i % (kMfAhead + 1)];
       const float ya = fmaf(xa, er[i], xb * en[i]);
       const float yb = fmaf(xa, -en[i], xb * er[i]);
