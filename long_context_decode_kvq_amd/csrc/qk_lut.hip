@@ -17,15 +17,18 @@
 // the pair's code field times 8, formed by one shift and one mask (two single-rate
 // integer operations, where a bit-field extract and a shift-add are two FMA-rate ones);
 // the row of the pair and the table buffer are immediate offsets of the read (the main
-// loop is unrolled over the two buffers).
+// loop is unrolled over the buffers).
 //
-// The waves of a block share the table of a super-tile.  Between two block barriers
-// every wave computes its tile of super-tile s and fills its rows of the table of s + 1
-// (double-buffered), the coefficients reaching the lanes by DPP row broadcasts; one wave
-// (a different one each step) forms the rotated-query coefficients of all 64 pairs for
-// s + 2.  Operands that come from LDS (the build coefficients, each outlier's scale,
-// frequency and rotated-query pair) are requested before the pair loop and consumed after
-// it, so their latency hides behind the loop.  Outliers replace the zero code decoded at
+// The waves of a block share the table of a super-tile.  With 3-bit keys, between two
+// block barriers every wave computes its tile of super-tile s and fills its rows of the
+// table of s + 1 (two buffers), and one wave (a different one each step) forms the
+// rotated-query coefficients of all 64 pairs for s + 2.  2-bit tables are small enough
+// for four buffers: a barrier every second step, the first of the two steps filling the
+// rows of s + 2 and s + 3 and forming the coefficients of s + 4 and s + 5.  The
+// coefficients reach the lanes by DPP row broadcasts.  Operands that come from LDS (the
+// build coefficients, each outlier's scale, frequency and rotated-query pair) are
+// requested before or early in the pair loop and consumed after it, so their latency
+// hides behind the loop.  Outliers replace the zero code decoded at
 // their channel: their correction uses the hardware sine/cosine (argument in revolutions)
 // at the outlier's pair.
 #include <algorithm>
@@ -53,8 +56,14 @@ struct LutShape {
   static constexpr int kBufBytes = kHalf * kRowBytes; // 64 rows
   // tables, build coefficients, rotated-query pairs, key scales, frequencies (split and
   // float64), query and scales per pair
-  static constexpr int kLdsBytes = 2 * kBufBytes + 2 * kHalf * 16 + 3 * kHalf * 8 + kHeadDim * 4 + kHalf * 8 +
-                                   kHalf * 16 + kHalf * 8;
+  // Steps per block barrier: 2-bit tables are small enough for four buffers, so a barrier
+  // every second step; 3-bit tables (32 KB each) keep two buffers and a barrier per step.
+  static constexpr int kSB = KB == 2 ? 2 : 1;
+  static constexpr int kNB = 2 * kSB;      // table buffers
+  static constexpr int kCR = 2 * kSB;      // build-coefficient ring
+  static constexpr int kPR = 4 * kSB;      // rotated-query ring of the outlier terms
+  static constexpr int kLdsBytes = kNB * kBufBytes + kCR * kHalf * 16 + kPR * kHalf * 8 + kHeadDim * 4 +
+                                   kHalf * 8 + kHalf * 16 + kHalf * 8;
 };
 
 template <int KB>
@@ -75,10 +84,11 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   // statically sized, so that table offsets are compile-time LDS addresses (immediate
   // offsets of the reads)
   __shared__ __align__(16) unsigned char lds[Sh::kLdsBytes];
-  float2* lut = reinterpret_cast<float2*>(lds);                           // [2][64][kNe] (A, B)
-  float4* coef = reinterpret_cast<float4*>(lds + 2 * Sh::kBufBytes);      // [2][64] (alpha, beta, gamma, -delta)
-  float2* cpab = reinterpret_cast<float2*>(coef + 2 * kHalf);             // [3][64] (p_a, p_b)
-  float* ks = reinterpret_cast<float*>(cpab + 3 * kHalf);                 // [128] key scales
+  constexpr int kSB = Sh::kSB, kNB = Sh::kNB, kCR = Sh::kCR, kPR = Sh::kPR;
+  float2* lut = reinterpret_cast<float2*>(lds);                           // [kNB][64][kNe] (A, B)
+  float4* coef = reinterpret_cast<float4*>(lds + kNB * Sh::kBufBytes);    // [kCR][64] (alpha, beta, gamma, -delta)
+  float2* cpab = reinterpret_cast<float2*>(coef + kCR * kHalf);           // [kPR][64] (p_a, p_b)
+  float* ks = reinterpret_cast<float*>(cpab + kPR * kHalf);               // [128] key scales
   float2* thl = reinterpret_cast<float2*>(ks + kHeadDim);                 // [64] theta_i/2pi split hi, lo
   float4* qsl = reinterpret_cast<float4*>(thl + kHalf);                   // [64] (q_i, q_{i+64}, s_i, s_{i+64})
   double* thd = reinterpret_cast<double*>(qsl + kHalf);                   // [64] theta_i/2pi
@@ -167,7 +177,7 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   const double th_ip = a.theta_rev[ip];
   const uint32_t cb_lane = a.k_cb[lane & (kNc - 1)];
 
-  LutRec<KB> r0, r1, r2;
+  LutRec<KB> r0, r1, r2, r3;  // r3 only with two steps per barrier
   load_rec(s_lo, r0);
   load_rec(s_lo + 1, r1);
 
@@ -206,8 +216,8 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
     const float cs = __builtin_amdgcn_cosf(r), sn = __builtin_amdgcn_sinf(r);
     const float pa = qs.x * cs + qs.y * sn;  // R(-t0 theta) q
     const float pb = qs.y * cs - qs.x * sn;
-    coef[(x & 1) * kHalf + lane] = make_float4(qs.z * pa, qs.z * pb, qs.w * pb, -(qs.w * pa));
-    cpab[(x % 3) * kHalf + lane] = make_float2(pa, pb);
+    coef[(x & (kCR - 1)) * kHalf + lane] = make_float4(qs.z * pa, qs.z * pb, qs.w * pb, -(qs.w * pa));
+    cpab[(x & (kPR - 1)) * kHalf + lane] = make_float2(pa, pb);
   };
 
   // ---- this wave's rows of the table of a super-tile into buffer B ---------------------
@@ -266,12 +276,18 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
     return dv * (o.lo_half ? (o.p.x * cs + o.p.y * sn) : (o.p.y * cs - o.p.x * sn));
   };
 
-  // ---- one tile of super-tile s from table buffer B, and the rows of s + 1 -------------
+  // ---- one tile of super-tile s from table buffer B --------------------------------------
+  // Every kSB-th step (B % kSB == 0) builds the tables of super-tiles s + kSB .. s + 2 kSB - 1
+  // and computes the coefficients of the kSB super-tiles after those; every step with
+  // B % kSB == kSB - 1 ends in the block barrier.  A table is thus finished one barrier before
+  // it is read, and a buffer or ring slot is rewritten only after a barrier that follows its
+  // last read.
   auto step = [&](auto bc, int s, const LutRec<KB>& d, LutRec<KB>& ahead) __attribute__((always_inline)) {
     constexpr int B = decltype(bc)::value;
-    const bool more = s + 1 < s_hi;
-    const float4 cc = coef[((s + 1) & 1) * kHalf + P];  // build coefficients of super-tile s + 1
-    const float2* pab = cpab + (s % 3) * kHalf;
+    constexpr bool kBuild = B % kSB == 0;
+    float4 cc[kSB];  // build coefficients of super-tiles s + kSB + j
+    if constexpr (kSB == 1) cc[0] = coef[((s + 1) & (kCR - 1)) * kHalf + P];
+    const float2* pab = cpab + (s & (kPR - 1)) * kHalf;
     OutOps o0, o1;
     if (kp >= 1) o0 = out_ops(d.oi[0], d.ov[0], pab);
     if (kp >= 2) o1 = out_ops(d.oi[1], d.ov[1], pab);
@@ -296,6 +312,10 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
       // scalar address arithmetic then overlaps the other wave's FMAs on this SIMD instead of
       // adding to the start of a step that both waves begin together after the barrier.
       if constexpr (i == 8) load_rec(s + 2, ahead);
+      if constexpr (kSB > 1 && kBuild && i == 40) {
+#pragma unroll
+        for (int j = 0; j < kSB; ++j) cc[j] = coef[((s + kSB + j) & (kCR - 1)) * kHalf + P];
+      }
       acc[i & 3] = fmaf(er[i], va[i % (kLutAhead + 1)], fmaf(ei[i], vb[i % (kLutAhead + 1)], acc[i & 3]));
       if constexpr ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     });
@@ -313,33 +333,57 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
       }
       (a.logits + (static_cast<size_t>(seq) * a.n_q_heads + kvh) * S + t0)[lane] = a.sm_scale * l;
     }
-    if (more) build(std::integral_constant<int, B ^ 1>{}, cc);
-    if (wave == s % kLutWaves && s + 2 < s_hi) coefs(s + 2);
-    block_lds_barrier();
+    if constexpr (kBuild) {
+      static_for<0, kSB>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if (s + kSB + j < s_hi) build(std::integral_constant<int, (B + kSB + j) % kNB>{}, cc[j]);
+      });
+#pragma unroll
+      for (int j = 0; j < kSB; ++j)
+        if (wave == ((s + j) & (kLutWaves - 1)) && s + 2 * kSB + j < s_hi) coefs(s + 2 * kSB + j);
+    }
+    if constexpr (B % kSB == kSB - 1) block_lds_barrier();
   };
 
   // ---- main loop -----------------------------------------------------------------------
   block_lds_barrier();  // qsl, thd, ks, thl visible
-  if (wave == 0) coefs(s_lo);
-  if (wave == 1 && s_lo + 1 < s_hi) coefs(s_lo + 1);
-  block_lds_barrier();  // the coefficients of the first two super-tiles visible
-  build(std::integral_constant<int, 0>{}, coef[(s_lo & 1) * kHalf + P]);
+  if (wave < 2 * kSB && s_lo + wave < s_hi) coefs(s_lo + wave);
+  block_lds_barrier();  // the coefficients of the first 2 kSB super-tiles visible
+  static_for<0, kSB>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if (s_lo + j < s_hi) build(std::integral_constant<int, j>{}, coef[((s_lo + j) & (kCR - 1)) * kHalf + P]);
+  });
   block_lds_barrier();
-  // six steps per round: three record sets (two super-tiles in flight) by two table buffers
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  for (int s = s_lo; s < s_hi; s += 6) {
-    step(I0{}, s, r0, r2);
-    if (s + 1 >= s_hi) break;
-    step(I1{}, s + 1, r1, r0);
-    if (s + 2 >= s_hi) break;
-    step(I0{}, s + 2, r2, r1);
-    if (s + 3 >= s_hi) break;
-    step(I1{}, s + 3, r0, r2);
-    if (s + 4 >= s_hi) break;
-    step(I0{}, s + 4, r1, r0);
-    if (s + 5 >= s_hi) break;
-    step(I1{}, s + 5, r2, r1);
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  if constexpr (kSB == 1) {
+    // six steps per round: three record sets (two super-tiles in flight) by two table buffers
+    for (int s = s_lo; s < s_hi; s += 6) {
+      step(I0{}, s, r0, r2);
+      if (s + 1 >= s_hi) break;
+      step(I1{}, s + 1, r1, r0);
+      if (s + 2 >= s_hi) break;
+      step(I0{}, s + 2, r2, r1);
+      if (s + 3 >= s_hi) break;
+      step(I1{}, s + 3, r0, r2);
+      if (s + 4 >= s_hi) break;
+      step(I0{}, s + 4, r1, r0);
+      if (s + 5 >= s_hi) break;
+      step(I1{}, s + 5, r2, r1);
+    }
+  } else {
+    // four steps per round: four record sets by four table buffers
+    for (int s = s_lo; s < s_hi; s += 4) {
+      step(I0{}, s, r0, r2);
+      if (s + 1 >= s_hi) break;
+      step(I1{}, s + 1, r1, r3);
+      if (s + 2 >= s_hi) break;
+      step(I2{}, s + 2, r2, r0);
+      if (s + 3 >= s_hi) break;
+      step(I3{}, s + 3, r3, r1);
+    }
   }
 }
 
