@@ -22,9 +22,9 @@
 // The waves of a block share the table of a super-tile.  With 3-bit keys, between two
 // block barriers every wave computes its tile of super-tile s and fills its rows of the
 // table of s + 1 (two buffers), and one wave (a different one each step) forms the
-// rotated-query coefficients of all 64 pairs for s + 2.  2-bit tables are small enough
-// for four buffers: a barrier every second step, the first of the two steps filling the
-// rows of s + 2 and s + 3 and forming the coefficients of s + 4 and s + 5.  The
+// rotated-query coefficients of all 64 pairs for s + 2.  2-bit tables (8 KB) are small
+// enough for eight buffers: a barrier every fourth step, the first of the four filling the
+// rows of s + 4 .. s + 7 and forming the coefficients of s + 8 .. s + 11.  The
 // coefficients reach the lanes by DPP row broadcasts.  Operands that come from LDS (the
 // build coefficients, each outlier's scale, frequency and rotated-query pair) are
 // requested before or early in the pair loop and consumed after it, so their latency
@@ -56,9 +56,9 @@ struct LutShape {
   static constexpr int kBufBytes = kHalf * kRowBytes; // 64 rows
   // tables, build coefficients, rotated-query pairs, key scales, frequencies (split and
   // float64), query and scales per pair
-  // Steps per block barrier: 2-bit tables are small enough for four buffers, so a barrier
-  // every second step; 3-bit tables (32 KB each) keep two buffers and a barrier per step.
-  static constexpr int kSB = KB == 2 ? 2 : 1;
+  // Steps per block barrier: 2-bit tables are small enough for eight buffers, so a barrier
+  // every fourth step; 3-bit tables (32 KB each) keep two buffers and a barrier per step.
+  static constexpr int kSB = KB == 2 ? 4 : 1;
   static constexpr int kNB = 2 * kSB;      // table buffers
   static constexpr int kCR = 2 * kSB;      // build-coefficient ring
   static constexpr int kPR = 4 * kSB;      // rotated-query ring of the outlier terms
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   const double th_ip = a.theta_rev[ip];
   const uint32_t cb_lane = a.k_cb[lane & (kNc - 1)];
 
-  LutRec<KB> r0, r1, r2, r3;  // r3 only with two steps per barrier
+  LutRec<KB> r0, r1, r2, r3;  // r3 only with several steps per barrier
   load_rec(s_lo, r0);
   load_rec(s_lo + 1, r1);
 
@@ -374,8 +374,12 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
       step(I1{}, s + 5, r2, r1);
     }
   } else {
-    // four steps per round: four record sets by four table buffers
-    for (int s = s_lo; s < s_hi; s += 4) {
+    // eight steps per round: four record sets by eight table buffers
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    using I6 = std::integral_constant<int, 6>;
+    using I7 = std::integral_constant<int, 7>;
+    for (int s = s_lo; s < s_hi; s += 8) {
       step(I0{}, s, r0, r2);
       if (s + 1 >= s_hi) break;
       step(I1{}, s + 1, r1, r3);
@@ -383,6 +387,14 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
       step(I2{}, s + 2, r2, r0);
       if (s + 3 >= s_hi) break;
       step(I3{}, s + 3, r3, r1);
+      if (s + 4 >= s_hi) break;
+      step(I4{}, s + 4, r0, r2);
+      if (s + 5 >= s_hi) break;
+      step(I5{}, s + 5, r1, r3);
+      if (s + 6 >= s_hi) break;
+      step(I6{}, s + 6, r2, r0);
+      if (s + 7 >= s_hi) break;
+      step(I7{}, s + 7, r3, r1);
     }
   }
 }
