@@ -10,8 +10,9 @@
 // tokens, tau < 64 kMfWaves) and rotary pair i with codes a (channel i) and b (i + 64):
 //   y_i = R(t theta_i) (cb[a] s_i, cb[b] s_{i+64}) = R(tau theta_i) X_i[a, b],
 //   X_i[a, b] = R(T0 theta_i) (cb[a] s_i, cb[b] s_{i+64}),
-// X a per-super-tile table of 64 rows of 2^(2b) float pairs (double-buffered, rows filled by
-// every wave between two block barriers, as in the one-head table kernel), E(tau) =
+// X a per-super-tile table of 64 rows of 2^(2b) float pairs (rows filled by every wave
+// between block barriers, as in the one-head table kernel: two buffers and a barrier per
+// step for 3-bit keys, eight buffers and a barrier every fourth step for 2-bit keys), E(tau) =
 // R(tau theta_i) in 128 registers (lane = token).  A key and pair cost the table address (a
 // shift and a mask), one 8-byte read, the rotation (four operations) and one conversion of
 // the rotated pair to fp16, independent of the number of heads.  The fp16 rotated keys are
@@ -59,19 +60,27 @@ struct MfShape {
   static constexpr int kGroups = G > 4 ? G / 4 : 1;   // MFMA row blocks of 4 heads
   static constexpr int kParts = kSplit ? 2 : 1;       // fp16 parts of the query
   static constexpr int kSteps = kHalf / 2;            // MFMA steps of 4 channels
-  // LDS layout (byte offsets): tables [2][64][kNe] float2; build coefficients [2][64]
-  // float4; rotated query pairs [3][G][64] float2; A operands [group][part][row][step] of 4
+  // LDS layout (byte offsets): tables [kNB][64][kNe] float2; build coefficients [kCR][64]
+  // float4; rotated query pairs [kPR][G][64] float2; A operands [group][part][row][step] of 4
   // fp16; query pairs [G][64] float2; per-head output scales [8]; key scales [128]; split
   // frequencies [64] float2
+  // Steps per block barrier (kSB): 2-bit tables are small enough for eight buffers (a
+  // barrier every fourth step) except where the extra record set would spill (eight heads,
+  // split fp32 queries); 3-bit tables (32 KB) keep two buffers and a barrier per step.
+  static constexpr int kSB = KB == 2 && !(G == 8 && kSplit) ? 4 : 1;
+  static constexpr int kNB = 2 * kSB;  // table buffers
+  static constexpr int kCR = 2 * kSB;  // build-coefficient ring
+  static constexpr int kPR = 4 * kSB;  // rotated-query ring
   static constexpr int kTab = 0;
-  static constexpr int kCoef = 2 * kBufBytes;
-  static constexpr int kCpab = kCoef + 2 * kHalf * 16;
-  static constexpr int kQa = kCpab + 3 * G * kHalf * 8;
+  static constexpr int kCoef = kNB * kBufBytes;
+  static constexpr int kCpab = kCoef + kCR * kHalf * 16;
+  static constexpr int kQa = kCpab + kPR * G * kHalf * 8;
   static constexpr int kQf = kQa + kGroups * kParts * 4 * kSteps * 8;
   static constexpr int kQsc = kQf + G * kHalf * 8;
   static constexpr int kKs = kQsc + 8 * 4;
   static constexpr int kThl = kKs + kHeadDim * 4;
   static constexpr int kLdsBytes = kThl + kHalf * 8;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS of one block");
 };
 
 template <int KB>
@@ -186,7 +195,7 @@ __global__ __launch_bounds__(kMfThreads) void qk_mfma_kernel(QkArgs a) {
   const double th_l = a.theta_rev[lane];
   const uint32_t cb_lane = a.k_cb[lane & (kNc - 1)];
 
-  MfRec<KB> r0, r1, r2;
+  MfRec<KB> r0, r1, r2, r3;  // r3 only with several steps per barrier
   load_rec(s_lo, r0);
   load_rec(s_lo + 1, r1);
 
@@ -263,11 +272,11 @@ __global__ __launch_bounds__(kMfThreads) void qk_mfma_kernel(QkArgs a) {
     const float r = frac_rev(t0, th_l);
     const float cs = __builtin_amdgcn_cosf(r), sn = __builtin_amdgcn_sinf(r);
     const float sa = s_lo_c * pre, sb = s_hi_c * pre;
-    coef[(x & 1) * kHalf + lane] = make_float4(cs * sa, sn * sa, -(sn * sb), cs * sb);
+    coef[(x & (Sh::kCR - 1)) * kHalf + lane] = make_float4(cs * sa, sn * sa, -(sn * sb), cs * sb);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float2 qq = qf[h * kHalf + lane];
-      cpab[((x % 3) * G + h) * kHalf + lane] = make_float2(qq.x * cs + qq.y * sn, qq.y * cs - qq.x * sn);
+      cpab[((x & (Sh::kPR - 1)) * G + h) * kHalf + lane] = make_float2(qq.x * cs + qq.y * sn, qq.y * cs - qq.x * sn);
     }
   };
 
@@ -335,9 +344,11 @@ __global__ __launch_bounds__(kMfThreads) void qk_mfma_kernel(QkArgs a) {
   // ---- one tile of super-tile s from table buffer B, and the rows of s + 1 -------------
   auto step = [&](auto bc, int s, const MfRec<KB>& d, MfRec<KB>& ahead) __attribute__((always_inline)) {
     constexpr int B = decltype(bc)::value;
-    const bool more = s + 1 < s_hi;
-    const float4 cc = coef[((s + 1) & 1) * kHalf + P];  // build coefficients of super-tile s + 1
-    const float2* pab = cpab + (s % 3) * G * kHalf;
+    constexpr int kSB = Sh::kSB, kNB = Sh::kNB, kCR = Sh::kCR, kPR = Sh::kPR;
+    constexpr bool kBuild = B % kSB == 0;
+    float4 cc[kSB];  // build coefficients of super-tiles s + kSB + j
+    if constexpr (kSB == 1) cc[0] = coef[((s + 1) & (kCR - 1)) * kHalf + P];
+    const float2* pab = cpab + (s & (kPR - 1)) * G * kHalf;
     OutOps o0, o1;
     if (kp >= 1) o0 = out_ops(d.oi[0], d.ov[0]);
     if (kp >= 2) o1 = out_ops(d.oi[1], d.ov[1]);
@@ -371,6 +382,10 @@ __global__ __launch_bounds__(kMfThreads) void qk_mfma_kernel(QkArgs a) {
       // the next records' loads and their scalar address arithmetic, issued inside the loop so
       // that they overlap the other wave's arithmetic rather than lengthen the step's start
       if constexpr (i == 8) load_rec(s + 2, ahead);
+      if constexpr (kSB > 1 && kBuild && i == 40) {
+#pragma unroll
+        for (int j = 0; j < kSB; ++j) cc[j] = coef[((s + kSB + j) & (kCR - 1)) * kHalf + P];
+      }
       const float xa = va[i % (kMfAhead + 1)], xb = vb[i % (kMfAhead + 1)];
       const float ya = fmaf(xa, er[i], xb * en[i]);
       const float yb = fmaf(xa, -en[i], xb * er[i]);
@@ -406,35 +421,72 @@ __global__ __launch_bounds__(kMfThreads) void qk_mfma_kernel(QkArgs a) {
 #pragma unroll
       for (int h = 0; h < G; ++h) lg[static_cast<size_t>(h) * S + lane] = fmaf(acc[h >> 2][h & 3], osc[h], a.sm_scale * ol[h]);
     }
-    if (more) build(std::integral_constant<int, B ^ 1>{}, cc);
-    if (wave == s % kMfWaves && s + 2 < s_hi) coefs(s + 2);
-    block_lds_barrier();
+    if constexpr (kBuild) {
+      static_for<0, kSB>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if (s + kSB + j < s_hi) build(std::integral_constant<int, (B + kSB + j) % kNB>{}, cc[j]);
+      });
+#pragma unroll
+      for (int j = 0; j < kSB; ++j)
+        if (wave == ((s + j) & (kMfWaves - 1)) && s + 2 * kSB + j < s_hi) coefs(s + 2 * kSB + j);
+    }
+    if constexpr (B % kSB == kSB - 1) block_lds_barrier();
   };
 
   // ---- main loop -----------------------------------------------------------------------
   block_lds_barrier();  // query pairs, A operands, scales, frequencies visible
 #pragma unroll
   for (int h = 0; h < G; ++h) osc[h] = a.sm_scale * pow2f(-pe) * (kSplit ? qsc[h] : 1.0f);
-  if (wave == 0) coefs(s_lo);
-  if (wave == 1 && s_lo + 1 < s_hi) coefs(s_lo + 1);
-  block_lds_barrier();  // the coefficients of the first two super-tiles visible
-  build(std::integral_constant<int, 0>{}, coef[(s_lo & 1) * kHalf + P]);
+  constexpr int kSB = Sh::kSB;
+  if (wave < 2 * kSB && s_lo + wave < s_hi) coefs(s_lo + wave);
+  block_lds_barrier();  // the coefficients of the first 2 kSB super-tiles visible
+  static_for<0, kSB>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if (s_lo + j < s_hi) build(std::integral_constant<int, j>{}, coef[((s_lo + j) & (Sh::kCR - 1)) * kHalf + P]);
+  });
   block_lds_barrier();
-  // six steps per round: three record sets (two super-tiles in flight) by two table buffers
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  for (int s = s_lo; s < s_hi; s += 6) {
-    step(I0{}, s, r0, r2);
-    if (s + 1 >= s_hi) break;
-    step(I1{}, s + 1, r1, r0);
-    if (s + 2 >= s_hi) break;
-    step(I0{}, s + 2, r2, r1);
-    if (s + 3 >= s_hi) break;
-    step(I1{}, s + 3, r0, r2);
-    if (s + 4 >= s_hi) break;
-    step(I0{}, s + 4, r1, r0);
-    if (s + 5 >= s_hi) break;
-    step(I1{}, s + 5, r2, r1);
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  if constexpr (kSB == 1) {
+    // six steps per round: three record sets (two super-tiles in flight) by two table buffers
+    for (int s = s_lo; s < s_hi; s += 6) {
+      step(I0{}, s, r0, r2);
+      if (s + 1 >= s_hi) break;
+      step(I1{}, s + 1, r1, r0);
+      if (s + 2 >= s_hi) break;
+      step(I0{}, s + 2, r2, r1);
+      if (s + 3 >= s_hi) break;
+      step(I1{}, s + 3, r0, r2);
+      if (s + 4 >= s_hi) break;
+      step(I0{}, s + 4, r1, r0);
+      if (s + 5 >= s_hi) break;
+      step(I1{}, s + 5, r2, r1);
+    }
+  } else {
+    // eight steps per round: four record sets by eight table buffers
+    using I4 = std::integral_constant<int, 4>;
+    using I5 = std::integral_constant<int, 5>;
+    using I6 = std::integral_constant<int, 6>;
+    using I7 = std::integral_constant<int, 7>;
+    for (int s = s_lo; s < s_hi; s += 8) {
+      step(I0{}, s, r0, r2);
+      if (s + 1 >= s_hi) break;
+      step(I1{}, s + 1, r1, r3);
+      if (s + 2 >= s_hi) break;
+      step(I2{}, s + 2, r2, r0);
+      if (s + 3 >= s_hi) break;
+      step(I3{}, s + 3, r3, r1);
+      if (s + 4 >= s_hi) break;
+      step(I4{}, s + 4, r0, r2);
+      if (s + 5 >= s_hi) break;
+      step(I5{}, s + 5, r1, r3);
+      if (s + 6 >= s_hi) break;
+      step(I6{}, s + 6, r2, r0);
+      if (s + 7 >= s_hi) break;
+      step(I7{}, s + 7, r3, r1);
+    }
   }
 }
 
