@@ -46,18 +46,34 @@ __device__ __forceinline__ float2 lut_entry_bcast(float al, float be, float ga, 
 }
 
 // Byte offset of rotary pair I's entry in a table row of 8-byte entries indexed by the
-// pair's 2KB-bit code field (a | b << KB): the field times 8, by a shift and a mask
-// (single-rate VOP2 operations; a field that straddles two words takes an align-bit
-// first).  W is the token's key record.
+// pair's 2KB-bit code field (a | b << KB): the field times 8.  W is the token's key record.
+//  - 2-bit codes (4-bit fields, eight to a word): the word's even fields times 8 are the
+//    bytes of (w << 3) & 0x78787878 and its odd fields times 8 those of (w >> 1) &
+//    0x78787878, two operations each shared by four pairs; a byte is then one AND (byte 0),
+//    one bit-field extract (bytes 1 and 2) or one shift (byte 3): 1.5 operations per pair.
+//  - 3-bit codes (6-bit fields): a shift and a mask per pair (an align-bit first for a
+//    field that straddles two words).
 template <int KB, int I, int N>
 __device__ __forceinline__ uint32_t pair_entry_offset(const uint32_t (&w)[N]) {
   constexpr int kBits = 2 * KB;
   constexpr int pos = kBits * I;
   constexpr int wi = pos / 32;
   constexpr int sh = pos % 32;
-  constexpr uint32_t mask = ((1u << kBits) - 1u) << 3;
   static_assert(wi < N, "field outside the record");
   uint32_t r;
+  if constexpr (KB == 2) {
+    constexpr int nib = I % 8;
+    constexpr int j = nib / 2;
+    const uint32_t src = (nib & 1) ? ((w[wi] >> 1) & 0x78787878u) : ((w[wi] << 3) & 0x78787878u);
+    if constexpr (j == 0)
+      asm("v_and_b32_e32 %0, 0xff, %1" : "=v"(r) : "v"(src));
+    else if constexpr (j == 3)
+      asm("v_lshrrev_b32_e32 %0, 24, %1" : "=v"(r) : "v"(src));
+    else
+      asm("v_bfe_u32 %0, %1, %2, 8" : "=v"(r) : "v"(src), "n"(8 * j));
+    return r;
+  }
+  constexpr uint32_t mask = ((1u << kBits) - 1u) << 3;
   if constexpr (sh + kBits <= 32) {
     if constexpr (sh >= 3) {
       asm("v_lshrrev_b32_e32 %0, %2, %1\n\tv_and_b32_e32 %0, %3, %0" : "=&v"(r) : "v"(w[wi]), "n"(sh - 3), "n"(mask));

@@ -14,10 +14,10 @@
 // where (p_a, p_b) = R(-T0 theta_i) (q_i, q_{i+64}) and E(tau) = (cos, sin)(tau theta_i).
 // Lane = token: each lane keeps E(tau) of its own tau for all 64 pairs in 128 registers,
 // so a pair costs one 8-byte table read, two FMAs and the table address.  The address is
-// the pair's code field times 8, formed by one shift and one mask (two single-rate
-// integer operations, where a bit-field extract and a shift-add are two FMA-rate ones);
-// the row of the pair and the table buffer are immediate offsets of the read (the main
-// loop is unrolled over the buffers).
+// the pair's code field times 8: 1.5 integer operations per pair for 2-bit codes (a word's
+// fields spread into bytes by two operations shared by four pairs, then one byte taken),
+// a shift and a mask for 3-bit codes; the row of the pair and the table buffer are
+// immediate offsets of the read (the main loop is unrolled over the buffers).
 //
 // The waves of a block share the table of a super-tile.  With 3-bit keys, between two
 // block barriers every wave computes its tile of super-tile s and fills its rows of the
