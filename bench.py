@@ -612,7 +612,7 @@ def main():
     dom = max(kt, key=kt.get)
     dom_bytes = {"qk": qk_bk, "pv": pv_bk}[dom]
     achieved = dom_bytes / (kt[dom] * 1e-3) / 1e9
-    qk_name = ("qk_kernel" if wl.k_bits == 4 else "qk_lut_kernel" if wl.group == 1 else "qk_mfma_kernel")
+    qk_name = ("qk_lut_kernel" if wl.group == 1 else "qk_kernel" if wl.k_bits == 4 else "qk_mfma_kernel")
     dom_name = {"qk": qk_name, "pv": "pv_partial_kernel+pv_combine_kernel"}[dom]
     # counted traffic is stored per workload as defined (another outlier count moves other bytes)
     traffic = (traffic_from_profile(args.workload, dom_name, source_hash(KERNEL_SOURCES[dom_name]))

@@ -254,10 +254,10 @@ int kvq_qk_matvec(const kvq_shape* s, const kvq_cache* c, const void* q, int32_t
   if (q_is_fp16 != 0 && q_is_fp16 != 1) return KVQ_ERR_INVALID;
   if (max_len < 1 || max_len > s->max_seq || !std::isfinite(sm_scale)) return KVQ_ERR_INVALID;
   const kvq::QkArgs a = make_qk_args(s, c, q, q_is_fp16, sm_scale, logits, max_len);
-  // 2- and 3-bit keys: the table-driven kernels, one query head per kv head (qk_lut) or
-  // grouped heads on the matrix cores (qk_mfma); 4-bit keys: the DPP kernel (with one head
-  // it measured faster than a table kernel: 120 against 134 us on the 128K layer).
-  if (s->n_q_heads == s->n_kv_heads && s->k_bits <= 3) return hip_status(kvq::launch_qk_lut(s->k_bits, s->batch, a, stream));
+  // One query head per kv head: the table kernel (qk_lut; 4-bit keys with separable rows);
+  // grouped heads: the matrix-core table kernel (qk_mfma) for 2/3-bit keys, the general
+  // kernel (qk) for 4-bit keys.
+  if (s->n_q_heads == s->n_kv_heads) return hip_status(kvq::launch_qk_lut(s->k_bits, s->batch, a, stream));
   if (s->k_bits <= 3) return hip_status(kvq::launch_qk_mfma(s->k_bits, s->n_q_heads / s->n_kv_heads, s->batch, a, stream));
   return hip_status(kvq::launch_qk(s->k_bits, s->n_q_heads / s->n_kv_heads, s->batch, a, stream));
 }

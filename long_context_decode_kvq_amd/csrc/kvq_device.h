@@ -89,6 +89,39 @@ __device__ __forceinline__ uint32_t pair_entry_offset(const uint32_t (&w)[N]) {
   return r;
 }
 
+// One separable 4-bit table entry (c0 cbv, c1 cbv), the coefficients from lane N of the
+// lane's 16-lane row by DPP row broadcast (sources written at least two wait states earlier).
+template <int N>
+__device__ __forceinline__ float2 lut_sep_bcast(float c0, float c1, float cbv) {
+  float A, B;
+  asm("v_mul_f32_dpp %0, %2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+      "v_mul_f32_dpp %1, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf bound_ctrl:1"
+      : "=&v"(A), "=&v"(B)
+      : "v"(c0), "v"(c1), "v"(cbv), "i"(N));
+  return make_float2(A, B);
+}
+
+// 4-bit codes: byte I of the record is pair I's field a | b << 4.  The even nibbles times 8
+// are the bytes of (w << 3) & 0x78787878, the odd ones those of (w >> 1) & 0x78787878; a
+// byte is one AND, bit-field extract or shift.  oa = 8 a, ob = 8 b.
+template <int I, int N>
+__device__ __forceinline__ void pair_offsets_sep4(const uint32_t (&w)[N], uint32_t& oa, uint32_t& ob) {
+  constexpr int wi = I / 4;
+  constexpr int j = I % 4;
+  static_assert(wi < N, "field outside the record");
+  const uint32_t lo = (w[wi] << 3) & 0x78787878u, hi = (w[wi] >> 1) & 0x78787878u;
+  if constexpr (j == 0) {
+    asm("v_and_b32_e32 %0, 0xff, %1" : "=v"(oa) : "v"(lo));
+    asm("v_and_b32_e32 %0, 0xff, %1" : "=v"(ob) : "v"(hi));
+  } else if constexpr (j == 3) {
+    asm("v_lshrrev_b32_e32 %0, 24, %1" : "=v"(oa) : "v"(lo));
+    asm("v_lshrrev_b32_e32 %0, 24, %1" : "=v"(ob) : "v"(hi));
+  } else {
+    asm("v_bfe_u32 %0, %1, %2, 8" : "=v"(oa) : "v"(lo), "n"(8 * j));
+    asm("v_bfe_u32 %0, %1, %2, 8" : "=v"(ob) : "v"(hi), "n"(8 * j));
+  }
+}
+
 // Wave reductions: four DPP steps combine the 16 lanes of each row (xor 1, xor 2, half-row
 // mirror, row mirror), then the four row results are read into scalar registers.  Every
 // lane gets the result; no LDS round trips.

@@ -14,17 +14,11 @@
 //   * R(tau), tau = lane < 64, from a per-block LDS table (with all 64 pairs in registers
 //     the kernel would drop to two waves per SIMD; 16 or 32 of them measured no faster).
 // The record keeps the two halves of rotary pair i side by side, so one 2b-bit field
-// indexes a small shared table of fp16 pairs (cb[a], cb[b]); the fp16 values feed
-// mixed-precision FMAs directly (exact conversion).  With one query head per kv head the
-// per-channel key scale is folded into four per-(tile, pair) coefficients of the rotated
-// query:
-//   l += cb[a] * (s_i q'_i E_r + s_i q'_{i+64} E_i) + cb[b] * (s_{i+64} q'_{i+64} E_r - s_{i+64} q'_i E_i)
-// (8 VALU ops per token and pair); the four coefficients reach the lanes through DPP row
-// broadcasts inside the multiplies, so the pair loop reads LDS only for the table lookup
-// (and R(tau) when it is not in registers).  With g > 1 query heads the key is dequantized
-// (the fp16 codebook pair scaled by the pair's two channel scales) and rotated once and
-// dotted with every head.  This kernel serves 4-bit keys; 2/3-bit keys go to the table
-// kernels (qk_lut.hip for one head per kv head, qk_mfma.hip for grouped heads).
+// indexes a small shared table of fp16 pairs (cb[a], cb[b]).  With g > 1 query heads the
+// key is dequantized (the fp16 codebook pair scaled by the pair's two channel scales),
+// rotated once and dotted with every head.  This kernel serves 4-bit keys with grouped
+// heads; one head per kv head goes to the table kernel (qk_lut.hip, every bit width) and
+// 2/3-bit grouped heads to the matrix-core kernel (qk_mfma.hip).
 #include <algorithm>
 #include <type_traits>
 
@@ -33,29 +27,6 @@
 
 namespace kvq {
 namespace {
-
-// One rotary pair's contribution for g = 1, in a single block so that the scheduler
-// keeps the six operations next to the table entry they consume:
-//   P = alpha E_r + beta E_i,  Q = gamma E_r + ndelta E_i,  acc += cb_a P + cb_b Q.
-// alpha, beta, gamma, ndelta are read from lane N of the lane's 16-lane row (DPP
-// row_newbcast), so one register per coefficient serves 16 pairs.  e2 holds the fp16
-// pair (cb_a, cb_b), consumed directly by the mixed-precision FMAs.  The DPP sources
-// must have been written at least two wait states earlier (see the fence where the
-// coefficients are formed).
-template <int N>
-__device__ __forceinline__ float pair_term(float acc, uint32_t e2, float er, float ei, float al, float be,
-                                           float ga, float nd) {
-  float p, q;
-  asm("v_mul_f32_dpp %1, %4, %8 row_newbcast:%10 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_mul_f32_dpp %2, %6, %8 row_newbcast:%10 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_fmac_f32_dpp %1, %5, %9 row_newbcast:%10 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_fmac_f32_dpp %2, %7, %9 row_newbcast:%10 row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-      "v_fma_mix_f32 %0, %3, %1, %0 op_sel_hi:[1,0,0]\n\t"
-      "v_fma_mix_f32 %0, %3, %2, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-      : "+v"(acc), "=&v"(p), "=&v"(q)
-      : "v"(e2), "v"(al), "v"(be), "v"(ga), "v"(nd), "v"(er), "v"(ei), "i"(N));
-  return acc;
-}
 
 constexpr int kWaves = 4;
 constexpr int kPrefetchOutliers = 2;  // outliers per token fetched with the record
@@ -71,8 +42,7 @@ template <int KB, int G>
 __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   constexpr int kNc = 1 << KB;
   constexpr int kPairEntries = 1 << (2 * KB);
-  static_assert(KB == 4, "4-bit keys (2/3-bit keys use the table kernels)");
-  constexpr bool kFoldScale = G == 1;
+  static_assert(KB == 4 && G > 1, "4-bit keys, grouped heads (the table kernels serve the rest)");
 
   __shared__ float2 et[kHalf][kTile];       // R(tau) for pair i: (cos, sin) of tau * theta_i
   using Tab = RepTable<kPairEntries>;
@@ -227,13 +197,10 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
   // value every outlier slot decodes to: the codebook entry nearest zero
   const float zc = zero_code_value<kNc>(cb_lo, lane);
   block_lds_barrier();
-  float s_lo[kSlots], s_hi[kSlots];  // scales of the slot pairs
-  float bc[kSlots], bs[kSlots], sc[kSlots], ss[kSlots];  // their tile-base phase and per-tile step
+  float bc[kSlots], bs[kSlots], sc[kSlots], ss[kSlots];  // slot pairs' tile-base phase and per-tile step
 #pragma unroll
   for (int j = 0; j < kSlots; ++j) {
     const int pr = (lane & 15) + 16 * j;
-    s_lo[j] = ks[pr];
-    s_hi[j] = ks[pr + kHalf];
     const float2 b = tb[wave][pr], st = tstep[pr];
     bc[j] = b.x;
     bs[j] = b.y;
@@ -252,7 +219,6 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
 
   auto process = [&](int tile, const Rec<KB>& d) {
     // q' = R(-t0) q for the slot pairs of every head, then step the base phases.
-    float alp[kSlots], bet[kSlots], gam[kSlots], ndl[kSlots];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       float pa[kSlots], pb[kSlots];
@@ -263,20 +229,6 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
       }
       const float pa_l = pick(pa[0], pa[1], pa[2], pa[3]), pb_l = pick(pb[0], pb[1], pb[2], pb[3]);
       qr[wave][h][lane] = make_float2(pa_l, pb_l);
-      if constexpr (kFoldScale) {
-#pragma unroll
-        for (int j = 0; j < kSlots; ++j) {
-          alp[j] = s_lo[j] * pa[j];
-          bet[j] = s_lo[j] * pb[j];
-          gam[j] = s_hi[j] * pb[j];
-          ndl[j] = -(s_hi[j] * pa[j]);
-        }
-        // at least two wait states between these VALU writes and their DPP reads
-        asm volatile("s_nop 1"
-                     : "+v"(alp[0]), "+v"(alp[1]), "+v"(alp[2]), "+v"(alp[3]), "+v"(bet[0]), "+v"(bet[1]),
-                       "+v"(bet[2]), "+v"(bet[3]), "+v"(gam[0]), "+v"(gam[1]), "+v"(gam[2]), "+v"(gam[3]),
-                       "+v"(ndl[0]), "+v"(ndl[1]), "+v"(ndl[2]), "+v"(ndl[3]));
-      }
     }
 #pragma unroll
     for (int j = 0; j < kSlots; ++j) {
@@ -296,45 +248,23 @@ __global__ __launch_bounds__(256) void qk_kernel(QkArgs a) {
 #pragma unroll
       for (int u = 0; u < kPartials; ++u) accp[h][u] = 0.0f;
 
-    // One head: the pair's table entry and R(tau) are requested kAhead pairs before their
-    // arithmetic (a rolling window of registers), so each wait leaves the later reads in
-    // flight; read just before use, every pair's wait drained all LDS reads (they complete
-    // in order).  Grouped heads also read their query pairs from LDS per pair and keep the
-    // reads beside their use.
-    constexpr int kAhead = kFoldScale ? 6 : 0;
-    uint32_t e2w[kAhead + 1];
-    float crw[kAhead + 1], ciw[kAhead + 1];
-    auto fetch = [&](auto ic) __attribute__((always_inline)) {
-      constexpr int i = decltype(ic)::value;
-      constexpr int r = i % (kAhead + 1);
-      e2w[r] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(lutp) +
-                                                  Tab::at(field<2 * KB, 2 * KB * i>(d.w), tab_base));
-      const float2 e = et[i][lane];  // R(tau) of pair i for this lane's token
-      crw[r] = e.x;
-      ciw[r] = e.y;
-    };
-    static_for<0, kAhead>([&](auto ic) { fetch(ic); });
+    // Per pair: the table entry (fp16 codebook pair), R(tau) and the heads' query pairs are
+    // read from LDS beside their use.
     static_for<0, kHalf>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      if constexpr (i + kAhead < kHalf) fetch(std::integral_constant<int, i + kAhead>{});
-      const uint32_t e2 = e2w[i % (kAhead + 1)];
-      const float cr = crw[i % (kAhead + 1)], ci = ciw[i % (kAhead + 1)];
-      if constexpr (kFoldScale) {
-        accp[0][i % kPartials] =
-            pair_term<i % 16>(accp[0][i % kPartials], e2, cr, ci, alp[i / 16], bet[i / 16], gam[i / 16], ndl[i / 16]);
-      } else {
-        const float2 sp = ksp[i];
-        const float xa = half_bits_to_float(e2 & 0xffffu) * sp.x;
-        const float xb = half_bits_to_float(e2 >> 16) * sp.y;
-        const float ya = xa * cr - xb * ci;
-        const float yb = xa * ci + xb * cr;
+      const uint32_t e2 = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(lutp) +
+                                                             Tab::at(field<2 * KB, 2 * KB * i>(d.w), tab_base));
+      const float2 e = et[i][lane];  // R(tau) of pair i for this lane's token
+      const float2 sp = ksp[i];
+      const float xa = half_bits_to_float(e2 & 0xffffu) * sp.x;
+      const float xb = half_bits_to_float(e2 >> 16) * sp.y;
+      const float ya = xa * e.x - xb * e.y;
+      const float yb = xa * e.y + xb * e.x;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float2 qq = qr[wave][h][i];
-          accp[h][i % kPartials] = fmaf(qq.y, yb, fmaf(qq.x, ya, accp[h][i % kPartials]));
-        }
+      for (int h = 0; h < G; ++h) {
+        const float2 qq = qr[wave][h][i];
+        accp[h][i % kPartials] = fmaf(qq.y, yb, fmaf(qq.x, ya, accp[h][i % kPartials]));
       }
-      if constexpr (kAhead > 0 && (i & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // keeps the reads ahead
     });
 
     float acc[G];
@@ -409,8 +339,8 @@ hipError_t launch_qk_t(int batch, const QkArgs& a0, hipStream_t s) {
 hipError_t launch_qk(int k_bits, int group, int batch, const QkArgs& a, hipStream_t s) {
 #define KVQ_QK_CASE(KB, G) \
   if (k_bits == KB && group == G) return launch_qk_t<KB, G>(batch, a, s);
-  // 2- and 3-bit keys go to the table kernels (qk_lut.hip, qk_mfma.hip)
-  KVQ_QK_CASE(4, 1) KVQ_QK_CASE(4, 2) KVQ_QK_CASE(4, 4) KVQ_QK_CASE(4, 8)
+  // 4-bit keys with grouped heads; the table kernels (qk_lut.hip, qk_mfma.hip) serve the rest
+  KVQ_QK_CASE(4, 2) KVQ_QK_CASE(4, 4) KVQ_QK_CASE(4, 8)
 #undef KVQ_QK_CASE
   return hipErrorInvalidValue;
 }

@@ -19,12 +19,20 @@
 // a shift and a mask for 3-bit codes; the row of the pair and the table buffer are
 // immediate offsets of the read (the main loop is unrolled over the buffers).
 //
+// 4-bit codes would need 256 entries per row; A and B are linear in cb[a] and cb[b], so
+// the row is stored separably instead: U[a] = cb[a] (s_i p_a, s_i p_b) and V[b] =
+// cb[b] (s_{i+64} p_b, -s_{i+64} p_a), 16 entries each, (A, B) = U[a] + V[b].  A pair then
+// costs two table reads, four FMAs and three address operations (byte i of the record is
+// the pair's field, its two nibbles spread as with 2-bit codes).  Its 16-register records
+// leave room for two record sets only, loaded one super-tile ahead.
+//
 // The waves of a block share the table of a super-tile.  With 3-bit keys, between two
 // block barriers every wave computes its tile of super-tile s and fills its rows of the
 // table of s + 1 (two buffers), and one wave (a different one each step) forms the
 // rotated-query coefficients of all 64 pairs for s + 2.  2-bit tables (8 KB) are small
 // enough for eight buffers: a barrier every fourth step, the first of the four filling the
-// rows of s + 4 .. s + 7 and forming the coefficients of s + 8 .. s + 11.  The
+// rows of s + 4 .. s + 7 and forming the coefficients of s + 8 .. s + 11; 4-bit tables
+// (16 KB) take four buffers and a barrier every second step in the same way.  The
 // coefficients reach the lanes by DPP row broadcasts.  Operands that come from LDS (the
 // build coefficients, each outlier's scale, frequency and rotated-query pair) are
 // requested before or early in the pair loop and consumed after it, so their latency
@@ -51,14 +59,17 @@ static_assert(kLutRows >= 4 && kLutRows <= 16, "a wave's rows are broadcast from
 template <int KB>
 struct LutShape {
   static constexpr int kNc = 1 << KB;
-  static constexpr int kNe = kNc * kNc;               // code pairs (a | b << KB) per rotary pair
+  // entries per row: one per code pair (a | b << KB) with 2/3-bit codes; with 4-bit codes
+  // the row is separable, 16 entries U[a] then 16 entries V[b]
+  static constexpr int kNe = KB == 4 ? 2 * kNc : kNc * kNc;
   static constexpr int kRowBytes = kNe * 8;           // (A, B) float pairs of one rotary pair
   static constexpr int kBufBytes = kHalf * kRowBytes; // 64 rows
   // tables, build coefficients, rotated-query pairs, key scales, frequencies (split and
   // float64), query and scales per pair
-  // Steps per block barrier: 2-bit tables are small enough for eight buffers, so a barrier
-  // every fourth step; 3-bit tables (32 KB each) keep two buffers and a barrier per step.
-  static constexpr int kSB = KB == 2 ? 4 : 1;
+  // Steps per block barrier: 2-bit tables (8 KB) in eight buffers, a barrier every fourth
+  // step; 4-bit separable tables (16 KB) in four buffers, every second step; 3-bit tables
+  // (32 KB) in two buffers, a barrier per step.
+  static constexpr int kSB = KB == 3 ? 1 : (KB == 4 ? 2 : 4);
   static constexpr int kNB = 2 * kSB;      // table buffers
   static constexpr int kCR = 2 * kSB;      // build-coefficient ring
   static constexpr int kPR = 4 * kSB;      // rotated-query ring of the outlier terms
@@ -74,12 +85,15 @@ struct LutRec {
 
 // kExtra: outliers beyond the first kLutPrefetchOutliers per token exist (read in a loop
 // of their own); without them that loop is compiled out.
+
 template <int KB, bool kExtra>
 __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   using Sh = LutShape<KB>;
   constexpr int kNc = Sh::kNc;
   constexpr int kNe = Sh::kNe;
-  static_assert(KB == 2 || KB == 3, "2- and 3-bit keys");
+  static_assert(KB >= 2 && KB <= 4, "2-, 3- and 4-bit keys");
+  // 4-bit records are 16 registers: two record sets, loaded one super-tile ahead
+  constexpr int kRecAhead = KB == 4 ? 1 : 2;
 
   // statically sized, so that table offsets are compile-time LDS addresses (immediate
   // offsets of the reads)
@@ -158,8 +172,11 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   // whose rows the wave fills, placed for the DPP row broadcasts of the build: 3-bit rows,
   // m = l mod kLutRows (lane m of every 16-lane row holds pair w + W m); 2-bit rows, lane
   // 16 r + f holds m = 4 f + r (fill step f finds its row's pair at lane f of the row).
-  const int P = KB == 3 ? wave + kLutWaves * (lane & (kLutRows - 1))
-                        : wave + kLutWaves * ((lane >> 4) + 4 * (lane & (kLutRows / 4 - 1)));
+  // 4-bit rows: lane 16 R + m holds pair 2 m + R / 2 (m < 4), U coefficients in even DPP
+  // rows R and V coefficients in odd ones.
+  const int P = KB == 3   ? wave + kLutWaves * (lane & (kLutRows - 1))
+                : KB == 2 ? wave + kLutWaves * ((lane >> 4) + 4 * (lane & (kLutRows / 4 - 1)))
+                          : wave + kLutWaves * ((2 * (lane & 15) + (lane >> 5)) & (kLutRows - 1));
   const int ip = tid & (kHalf - 1);
   const size_t qbase = (static_cast<size_t>(seq) * a.n_q_heads + kvh) * kHeadDim;
   uint32_t qraw[2];
@@ -177,9 +194,9 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   const double th_ip = a.theta_rev[ip];
   const uint32_t cb_lane = a.k_cb[lane & (kNc - 1)];
 
-  LutRec<KB> r0, r1, r2, r3;  // r3 only with several steps per barrier
+  LutRec<KB> r0, r1, r2, r3;  // r2 and r3 only with several record sets
   load_rec(s_lo, r0);
-  load_rec(s_lo + 1, r1);
+  if constexpr (kRecAhead == 2) load_rec(s_lo + 1, r1);
 
   if (tid < kHalf) {
     float qv[2];
@@ -193,7 +210,7 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
   }
   const float zc = zero_code_value<kNc>(cb_lane, lane);  // value every outlier slot decodes to
   // codebook values this lane's table entries use: entry e = a | b << KB
-  const int e0 = KB == 3 ? lane : (lane & 15);
+  const int e0 = KB == 3 ? lane : (lane & 15);  // 4-bit: cba = cb[lane & 15], the lane's U or V entry
   const float cba = half_bits_to_float(__shfl(static_cast<int>(cb_lane), e0 & (kNc - 1)) & 0xffffu);
   const float cbb = half_bits_to_float(__shfl(static_cast<int>(cb_lane), (e0 >> KB) & (kNc - 1)) & 0xffffu);
 
@@ -233,7 +250,7 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
         constexpr int m = decltype(mc)::value;
         T[(wave + kLutWaves * m) * kNe + lane] = lut_entry_bcast<m>(cc.x, cc.y, cc.z, cc.w, cba, cbb);
       });
-    } else {
+    } else if constexpr (KB == 2) {
       // 16 entries per row: fill step f covers the rows of 4 pairs, m = 4 f + (lane >> 4),
       // whose coefficients lane f of each 16-lane row holds (DPP row broadcast).
       asm volatile("s_nop 1" : "+v"(cc.x), "+v"(cc.y), "+v"(cc.z), "+v"(cc.w));  // DPP read wait states
@@ -241,6 +258,19 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
         constexpr int f = decltype(fc)::value;
         const int i = wave + kLutWaves * (4 * f + (lane >> 4));
         T[i * kNe + (lane & 15)] = lut_entry_bcast<f>(cc.x, cc.y, cc.z, cc.w, cba, cbb);
+      });
+    } else {
+      // separable rows: U[a] = cb[a] (alpha, beta), V[b] = cb[b] (gamma, -delta).  Fill
+      // step f covers pairs 2 f (lanes 0..31) and 2 f + 1 (lanes 32..63); a 16-lane row
+      // holds U or V entries only, so lane f of the row broadcasts the one coefficient pair
+      // it needs.
+      const bool v_row = (lane >> 4) & 1;
+      float c0 = v_row ? cc.z : cc.x, c1 = v_row ? cc.w : cc.y;
+      asm volatile("s_nop 1" : "+v"(c0), "+v"(c1));  // DPP read wait states
+      static_for<0, kLutRows / 2>([&](auto fc) {
+        constexpr int f = decltype(fc)::value;
+        const int i = wave + kLutWaves * (2 * f + (lane >> 5));
+        T[i * kNe + (lane & 31)] = lut_sep_bcast<f>(c0, c1, cba);
       });
     }
   };
@@ -298,11 +328,23 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
     const unsigned char* tb = lds + B * Sh::kBufBytes;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     float va[kLutAhead + 1], vb[kLutAhead + 1];
+    float wa[KB == 4 ? kLutAhead + 1 : 1], wb[KB == 4 ? kLutAhead + 1 : 1];  // 4-bit: V[b]
     auto issue = [&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      const float2 v = *reinterpret_cast<const float2*>(tb + i * Sh::kRowBytes + pair_entry_offset<KB, i>(d.w));
-      va[i % (kLutAhead + 1)] = v.x;
-      vb[i % (kLutAhead + 1)] = v.y;
+      if constexpr (KB == 4) {
+        uint32_t oa, ob;
+        pair_offsets_sep4<i>(d.w, oa, ob);
+        const float2 u = *reinterpret_cast<const float2*>(tb + i * Sh::kRowBytes + oa);
+        const float2 v = *reinterpret_cast<const float2*>(tb + i * Sh::kRowBytes + 8 * kNc + ob);
+        va[i % (kLutAhead + 1)] = u.x;
+        vb[i % (kLutAhead + 1)] = u.y;
+        wa[i % (kLutAhead + 1)] = v.x;
+        wb[i % (kLutAhead + 1)] = v.y;
+      } else {
+        const float2 v = *reinterpret_cast<const float2*>(tb + i * Sh::kRowBytes + pair_entry_offset<KB, i>(d.w));
+        va[i % (kLutAhead + 1)] = v.x;
+        vb[i % (kLutAhead + 1)] = v.y;
+      }
     };
     static_for<0, kLutAhead>([&](auto ic) { issue(ic); });
     static_for<0, kHalf>([&](auto ic) {
@@ -311,12 +353,19 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
       // The record loads of super-tile s + 2 go out here rather than at the step start: their
       // scalar address arithmetic then overlaps the other wave's FMAs on this SIMD instead of
       // adding to the start of a step that both waves begin together after the barrier.
-      if constexpr (i == 8) load_rec(s + 2, ahead);
+      if constexpr (i == 8) load_rec(s + kRecAhead, ahead);
       if constexpr (kSB > 1 && kBuild && i == 40) {
 #pragma unroll
         for (int j = 0; j < kSB; ++j) cc[j] = coef[((s + kSB + j) & (kCR - 1)) * kHalf + P];
       }
-      acc[i & 3] = fmaf(er[i], va[i % (kLutAhead + 1)], fmaf(ei[i], vb[i % (kLutAhead + 1)], acc[i & 3]));
+      if constexpr (KB == 4) {
+        acc[0] = fmaf(er[i], va[i % (kLutAhead + 1)], acc[0]);
+        acc[1] = fmaf(ei[i], vb[i % (kLutAhead + 1)], acc[1]);
+        acc[2] = fmaf(er[i], wa[i % (kLutAhead + 1)], acc[2]);
+        acc[3] = fmaf(ei[i], wb[i % (kLutAhead + 1)], acc[3]);
+      } else {
+        acc[i & 3] = fmaf(er[i], va[i % (kLutAhead + 1)], fmaf(ei[i], vb[i % (kLutAhead + 1)], acc[i & 3]));
+      }
       if constexpr ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     });
     float l = (acc[0] + acc[1]) + (acc[2] + acc[3]);
@@ -373,8 +422,21 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
       if (s + 5 >= s_hi) break;
       step(I1{}, s + 5, r2, r1);
     }
+  } else if constexpr (kRecAhead == 1) {
+    static_assert(kNB == 4, "buffer count");
+    // four steps per round: two record sets by four table buffers
+    for (int s = s_lo; s < s_hi; s += 4) {
+      step(I0{}, s, r0, r1);
+      if (s + 1 >= s_hi) break;
+      step(I1{}, s + 1, r1, r0);
+      if (s + 2 >= s_hi) break;
+      step(I2{}, s + 2, r0, r1);
+      if (s + 3 >= s_hi) break;
+      step(I3{}, s + 3, r1, r0);
+    }
   } else {
     // eight steps per round: four record sets by eight table buffers
+    static_assert(kNB == 8, "buffer count");
     using I4 = std::integral_constant<int, 4>;
     using I5 = std::integral_constant<int, 5>;
     using I6 = std::integral_constant<int, 6>;
@@ -428,6 +490,7 @@ hipError_t launch_qk_lut(int k_bits, int batch, const QkArgs& a, hipStream_t s) 
   const bool extra = a.n_outliers > kLutPrefetchOutliers;
   if (k_bits == 2) return extra ? launch_qk_lut_t<2, true>(batch, a, s) : launch_qk_lut_t<2, false>(batch, a, s);
   if (k_bits == 3) return extra ? launch_qk_lut_t<3, true>(batch, a, s) : launch_qk_lut_t<3, false>(batch, a, s);
+  if (k_bits == 4) return extra ? launch_qk_lut_t<4, true>(batch, a, s) : launch_qk_lut_t<4, false>(batch, a, s);
   return hipErrorInvalidValue;
 }
 

@@ -55,6 +55,9 @@ CASES = {
     # the second, with one head and with grouped heads
     "mha2_4bit_k5": (_wl("llama7b_128k_4bit", n_q_heads=2, n_kv_heads=2, seq_len=1100, outlier_frac=0.035),
                      [1100], None),
+    # one head with 4-bit keys (separable table rows) and fp32 queries, ragged batch
+    "mha2_4bit_q32_batch": (_wl("llama7b_128k_4bit", batch=3, n_q_heads=2, n_kv_heads=2, seq_len=1300, q_dtype="fp32"),
+                            [1300, 517, 1], None),
     "gqa2_4bit_k5": (_wl("llama7b_128k_4bit", batch=2, n_q_heads=4, n_kv_heads=2, seq_len=700, outlier_frac=0.035),
                      [700, 131], None),
     # grouped heads with 2-bit keys (the per-pair table path of the general kernel)
