@@ -8,9 +8,10 @@ outlier indices/values and value scales bit for bit over every token, and for ev
 query head of the stream's group every logit (|dl| <= 1e-3 sm sum_c |q_c y_c|) and the
 output (|do| <= 1e-3 sum_t p_t |v~_t|).  Sizes: the LLaMA-7B-shaped layer at 32K tokens
 (3-bit), 128K (4-bit, Laplace outlier channels) and 1M (2-bit), and the Llama-3-8B-shaped
-GQA layer (batch 16, 32 query heads on 8 kv heads, 64K tokens each), and the 32K layer
-again under the per-channel key outlier rule; the oracle needs about a minute of host
-time for the 1M stream.
+GQA layer (batch 16, 32 query heads on 8 kv heads, 64K tokens each), the 32K layer
+again under the per-channel key outlier rule, and the 1M and 128K shapes cut to 27K
+tokens, where the one-head q.K^T blocks end part-way through their rounds between
+barriers; the oracle needs about a minute of host time for the 1M stream.
 """
 import math
 
@@ -34,14 +35,21 @@ SAMPLED = {
     "llama3_8b_gqa_b16_64k": [(0, 0), (9, 5), (15, 7)],
     # the per-channel key outlier rule, each channel's scale the 0.99 quantile of |key|
     "llama7b_32k@per_channel": [(0, 3), (0, 30)],
+    # 53 super-tiles of 512 tokens per head over 8 blocks per head: blocks of 7 steps and
+    # one of 4, so the one-head q.K^T leaves its 4-step (2-bit) and 2-step (4-bit) rounds
+    # between block barriers part-way, with 2 and 4 record sets
+    "llama7b_1m_2bit@27k": [(0, 4), (0, 27)],
+    "llama7b_128k_4bit@27k": [(0, 2), (0, 19)],
 }
+# shape overrides of the variants above
+VARIANTS = {"llama7b_1m_2bit@27k": dict(seq_len=27036), "llama7b_128k_4bit@27k": dict(seq_len=27036)}
 
 
 @pytest.mark.parametrize("name", sorted(SAMPLED))
 def test_full_layer_sampled_heads(name):
     import long_context_decode_kvq_amd as kvq
     per_channel = name.endswith("@per_channel")
-    wl = synth.WORKLOADS[name.split("@")[0]]
+    wl = synth.WORKLOADS[name.split("@")[0]].with_(**VARIANTS.get(name, {}))
     seed = 0
     L0 = wl.seq_len
     n = L0 + 1  # the prompt plus one decode-step token
