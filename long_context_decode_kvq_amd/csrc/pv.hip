@@ -381,34 +381,74 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
       float accp[G][2][2];
   #pragma unroll
       for (int h = 0; h < G; ++h) accp[h][0][0] = accp[h][0][1] = accp[h][1][0] = accp[h][1][1] = 0.0f;
-      if constexpr (kQuad) {
-        static_for<0, kTile / 4>([&](auto qc) {
-          constexpr int qq = decltype(qc)::value;
-          const uint2 e0 = lut4[field<4 * VB, 4 * VB * qq>(d.w)];
-          const uint2 e1 = lut4[field<4 * VB, kChanBits + 4 * VB * qq>(d.w)];
+      // A step is the tokens one table entry covers (four with 2-bit values, else two) for
+      // both channels of the lane.  Table reads go in groups of two steps (four reads),
+      // issued four steps ahead, and a group's products take its last read first, so one
+      // LDS wait covers the group (a wait per read measured slower).
+      constexpr int kSteps = kQuad ? kTile / 4 : kTile / 2;
+      constexpr int kGS = 2;
+      constexpr int kAheadS = 4;
+      constexpr int kRingS = kAheadS + kGS;
+      uint2 r0[kRingS], r1[kRingS];
+      auto issue = [&](auto sc) __attribute__((always_inline)) {
+        constexpr int q = decltype(sc)::value;
+        if constexpr (kQuad) {
+          r0[q % kRingS] = lut4[field<4 * VB, 4 * VB * q>(d.w)];
+          r1[q % kRingS] = lut4[field<4 * VB, kChanBits + 4 * VB * q>(d.w)];
+        } else {
+          r0[q % kRingS].x = lut2[field<2 * VB, 2 * VB * q>(d.w)];
+          r1[q % kRingS].x = lut2[field<2 * VB, kChanBits + 2 * VB * q>(d.w)];
+        }
+      };
+      // weight pairs of a group, read one group ahead (a lane read's result needs wait
+      // states before a VALU instruction can use it)
+      constexpr int kWG = kQuad ? 2 * kGS : kGS;  // weight pairs per group
+      uint32_t wr[G][2 * kWG];
+      auto wload = [&](auto gc) __attribute__((always_inline)) {
+        constexpr int g = decltype(gc)::value;
+        static_for<0, kWG>([&](auto jc) {
+          constexpr int m = kWG * g + decltype(jc)::value;
   #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const half2_t wlo = __builtin_bit_cast(half2_t, wpair_of(h, std::integral_constant<int, 2 * qq>{}));
-            const half2_t whi = __builtin_bit_cast(half2_t, wpair_of(h, std::integral_constant<int, 2 * qq + 1>{}));
-            accp[h][0][0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e0.x), wlo, accp[h][0][0], false);
-            accp[h][0][1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e0.y), whi, accp[h][0][1], false);
-            accp[h][1][0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e1.x), wlo, accp[h][1][0], false);
-            accp[h][1][1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e1.y), whi, accp[h][1][1], false);
-          }
+          for (int h = 0; h < G; ++h) wr[h][m % (2 * kWG)] = wpair_of(h, std::integral_constant<int, m>{});
         });
-      } else {
-        static_for<0, kTile / 2>([&](auto mc) {
-          constexpr int mm = decltype(mc)::value;
-          const half2_t e0 = __builtin_bit_cast(half2_t, lut2[field<2 * VB, 2 * VB * mm>(d.w)]);
-          const half2_t e1 = __builtin_bit_cast(half2_t, lut2[field<2 * VB, kChanBits + 2 * VB * mm>(d.w)]);
+      };
+      // channel half hf of step q
+      auto consume = [&](auto sc, auto hc) __attribute__((always_inline)) {
+        constexpr int q = decltype(sc)::value;
+        constexpr int hf = decltype(hc)::value;
+        const uint2 e = hf ? r1[q % kRingS] : r0[q % kRingS];
   #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const half2_t wp = __builtin_bit_cast(half2_t, wpair_of(h, mc));
-            accp[h][0][mm & 1] = __builtin_amdgcn_fdot2(e0, wp, accp[h][0][mm & 1], false);
-            accp[h][1][mm & 1] = __builtin_amdgcn_fdot2(e1, wp, accp[h][1][mm & 1], false);
+        for (int h = 0; h < G; ++h) {
+          if constexpr (kQuad) {
+            const half2_t wlo = __builtin_bit_cast(half2_t, wr[h][(2 * q) % (2 * kWG)]);
+            const half2_t whi = __builtin_bit_cast(half2_t, wr[h][(2 * q + 1) % (2 * kWG)]);
+            accp[h][hf][0] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e.x), wlo, accp[h][hf][0], false);
+            accp[h][hf][1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e.y), whi, accp[h][hf][1], false);
+          } else {
+            const half2_t wp = __builtin_bit_cast(half2_t, wr[h][q % (2 * kWG)]);
+            accp[h][hf][q & 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, e.x), wp, accp[h][hf][q & 1], false);
           }
+        }
+      };
+      using Z = std::integral_constant<int, 0>;
+      using O = std::integral_constant<int, 1>;
+      static_for<0, kAheadS>([&](auto sc) { issue(sc); });
+      wload(Z{});
+      static_for<0, kSteps / kGS>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        static_for<0, kGS>([&](auto jc) {
+          constexpr int q = kGS * g + kAheadS + decltype(jc)::value;
+          if constexpr (q < kSteps) issue(std::integral_constant<int, q>{});
         });
-      }
+        if constexpr (g + 1 < kSteps / kGS) wload(std::integral_constant<int, g + 1>{});
+        consume(std::integral_constant<int, kGS * g + kGS - 1>{}, O{});
+        consume(std::integral_constant<int, kGS * g + kGS - 1>{}, Z{});
+        static_for<0, kGS - 1>([&](auto jc) {
+          consume(std::integral_constant<int, kGS * g + decltype(jc)::value>{}, Z{});
+          consume(std::integral_constant<int, kGS * g + decltype(jc)::value>{}, O{});
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
   #pragma unroll
       for (int h = 0; h < G; ++h) {
         acc[h][0] = fmaf(accp[h][0][0] + accp[h][0][1], unsc[h], acc[h][0]);

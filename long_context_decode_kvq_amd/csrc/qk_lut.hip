@@ -52,7 +52,6 @@ constexpr int kLutWaves = 8;                 // waves per block = tiles per supe
 constexpr int kLutThreads = 64 * kLutWaves;
 constexpr int kLutSuper = kLutWaves * kTile; // tokens per super-tile
 constexpr int kLutPrefetchOutliers = 2;      // outliers per token fetched with the record
-constexpr int kLutAhead = 7;                 // table reads in flight ahead of the FMAs (at most 15)
 constexpr int kLutRows = kHalf / kLutWaves;  // table rows (rotary pairs) each wave fills
 static_assert(kLutRows >= 4 && kLutRows <= 16, "a wave's rows are broadcast from lanes 0..15 of a DPP row");
 
@@ -322,13 +321,18 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
     if (kp >= 1) o0 = out_ops(d.oi[0], d.ov[0], pab);
     if (kp >= 2) o1 = out_ops(d.oi[1], d.ov[1], pab);
 
-    // Rolling window over the 64 pairs: the table read of pair i + kLutAhead is issued
-    // before the FMAs of pair i, so each read has kLutAhead pairs of arithmetic to arrive
-    // in (the scheduling barriers keep that order).
+    // The 64 pairs in groups of four: the table reads of the group kAhead pairs further on
+    // are issued before the FMAs of this group, and those FMAs take the group's last read
+    // first, so one LDS wait covers the group's four reads (a wait per read left the two
+    // waves of a SIMD issuing waits together a sixth of the time).  The scheduling barriers
+    // keep that order.
     const unsigned char* tb = lds + B * Sh::kBufBytes;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float va[kLutAhead + 1], vb[kLutAhead + 1];
-    float wa[KB == 4 ? kLutAhead + 1 : 1], wb[KB == 4 ? kLutAhead + 1 : 1];  // 4-bit: V[b]
+    // pairs read ahead: 4-bit pairs take two reads each, and eight more registers would spill
+    constexpr int kAhead = KB == 4 ? 4 : 8;
+    constexpr int kRing = kAhead + 4;
+    float va[kRing], vb[kRing];
+    float wa[KB == 4 ? kRing : 1], wb[KB == 4 ? kRing : 1];  // 4-bit: V[b]
     auto issue = [&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
       if constexpr (KB == 4) {
@@ -336,37 +340,48 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
         pair_offsets_sep4<i>(d.w, oa, ob);
         const float2 u = *reinterpret_cast<const float2*>(tb + i * Sh::kRowBytes + oa);
         const float2 v = *reinterpret_cast<const float2*>(tb + i * Sh::kRowBytes + 8 * kNc + ob);
-        va[i % (kLutAhead + 1)] = u.x;
-        vb[i % (kLutAhead + 1)] = u.y;
-        wa[i % (kLutAhead + 1)] = v.x;
-        wb[i % (kLutAhead + 1)] = v.y;
+        va[i % kRing] = u.x;
+        vb[i % kRing] = u.y;
+        wa[i % kRing] = v.x;
+        wb[i % kRing] = v.y;
       } else {
         const float2 v = *reinterpret_cast<const float2*>(tb + i * Sh::kRowBytes + pair_entry_offset<KB, i>(d.w));
-        va[i % (kLutAhead + 1)] = v.x;
-        vb[i % (kLutAhead + 1)] = v.y;
+        va[i % kRing] = v.x;
+        vb[i % kRing] = v.y;
       }
     };
-    static_for<0, kLutAhead>([&](auto ic) { issue(ic); });
-    static_for<0, kHalf>([&](auto ic) {
+    auto consume = [&](auto ic) __attribute__((always_inline)) {
       constexpr int i = decltype(ic)::value;
-      if constexpr (i + kLutAhead < kHalf) issue(std::integral_constant<int, i + kLutAhead>{});
+      constexpr int r = i % kRing;
+      if constexpr (KB == 4) {
+        acc[0] = fmaf(er[i], va[r], acc[0]);
+        acc[1] = fmaf(ei[i], vb[r], acc[1]);
+        acc[2] = fmaf(er[i], wa[r], acc[2]);
+        acc[3] = fmaf(ei[i], wb[r], acc[3]);
+      } else {
+        acc[i & 3] = fmaf(er[i], va[r], fmaf(ei[i], vb[r], acc[i & 3]));
+      }
+    };
+    static_for<0, kAhead>([&](auto ic) { issue(ic); });
+    static_for<0, kHalf / 4>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      static_for<0, 4>([&](auto jc) {
+        constexpr int i = 4 * g + kAhead + decltype(jc)::value;
+        if constexpr (i < kHalf) issue(std::integral_constant<int, i>{});
+      });
       // The record loads of super-tile s + 2 go out here rather than at the step start: their
       // scalar address arithmetic then overlaps the other wave's FMAs on this SIMD instead of
       // adding to the start of a step that both waves begin together after the barrier.
-      if constexpr (i == 8) load_rec(s + kRecAhead, ahead);
-      if constexpr (kSB > 1 && kBuild && i == 40) {
+      if constexpr (g == 2) load_rec(s + kRecAhead, ahead);
+      if constexpr (kSB > 1 && kBuild && g == 10) {
 #pragma unroll
         for (int j = 0; j < kSB; ++j) cc[j] = coef[((s + kSB + j) & (kCR - 1)) * kHalf + P];
       }
-      if constexpr (KB == 4) {
-        acc[0] = fmaf(er[i], va[i % (kLutAhead + 1)], acc[0]);
-        acc[1] = fmaf(ei[i], vb[i % (kLutAhead + 1)], acc[1]);
-        acc[2] = fmaf(er[i], wa[i % (kLutAhead + 1)], acc[2]);
-        acc[3] = fmaf(ei[i], wb[i % (kLutAhead + 1)], acc[3]);
-      } else {
-        acc[i & 3] = fmaf(er[i], va[i % (kLutAhead + 1)], fmaf(ei[i], vb[i % (kLutAhead + 1)], acc[i & 3]));
-      }
-      if constexpr ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+      consume(std::integral_constant<int, 4 * g + 3>{});
+      consume(std::integral_constant<int, 4 * g>{});
+      consume(std::integral_constant<int, 4 * g + 1>{});
+      consume(std::integral_constant<int, 4 * g + 2>{});
+      __builtin_amdgcn_sched_barrier(0);
     });
     float l = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     // Outliers: the record holds the zero code at each outlier channel; replace its decoded
