@@ -323,9 +323,8 @@ __global__ __launch_bounds__(kLutThreads) void qk_lut_kernel(QkArgs a) {
 
     // The 64 pairs in groups of four: the table reads of the group kAhead pairs further on
     // are issued before the FMAs of this group, and those FMAs take the group's last read
-    // first, so one LDS wait covers the group's four reads (a wait per read left the two
-    // waves of a SIMD issuing waits together a sixth of the time).  The scheduling barriers
-    // keep that order.
+    // first, so one LDS wait covers the group's four reads (a wait before every pair's FMAs
+    // measured 2-5 % slower).  The scheduling barriers keep that order.
     const unsigned char* tb = lds + B * Sh::kBufBytes;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     // pairs read ahead: 4-bit pairs take two reads each, and eight more registers would spill
