@@ -376,3 +376,61 @@ def test_pv_split_merge_across_calls_on_one_workspace(name):
                 ref, scale = expected[sign, hq]
                 assert_out_close(got[0, hq], ref, scale, what=f"{name} it={it} sign={sign} hq={hq}")
             assert np.all(got[1] == 0.0), f"{name}: empty sequence output not zero"
+
+
+def _logit_patterns(n: int, rng) -> dict:
+    """Logit sequences that move a running softmax max in different ways: slow and steep
+    ramps (the max rises on every tile; with slope 0.2 weights relative to a max set one
+    tile earlier reach e^12.8), a fall, single spikes just under and far over 16 above the
+    rest, steps of +-40 between tiles, and tiles alternating between 0 and 15.9 (weights
+    near e^15.9 on every other tile of each wave when the max is not raised)."""
+    t = np.arange(n, dtype=np.float64)
+    noise = rng.normal(size=n)
+    return {
+        "ramp_0.2": 0.2 * t,
+        "ramp_1": 1.0 * t,
+        "fall": -0.5 * t,
+        "spike_15.9": noise + 15.9 * (t == n // 2),
+        "spike_30": noise + 30.0 * (t == n // 3),
+        "steps": 40.0 * ((t // 64) % 3 - 1) + noise,
+        "sawtooth_15.9": 15.9 * ((t // 64) % 2),
+    }
+
+
+@pytest.mark.parametrize("name", ["g1", "g4", "g8"])
+def test_pv_running_max_under_logit_ramps_and_spikes(name):
+    """softmax.V keeps a running max per wave; with one query head it is raised only when a
+    logit exceeds it by more than 16, so weights reach e^16, and grouped heads share one
+    fixed-point outlier scale.  Logit patterns fed directly (a different one per head of a
+    group, so within a tile the heads' weights differ by many orders of magnitude) must
+    give the oracle's attention over the same float32 logits."""
+    import long_context_decode_kvq_amd as kvq
+    wl, lens = MERGE_CASES[name]
+    case = Case(wl, seed=11, lens=lens, device="cuda")
+    cache = case.build_gpu()
+    n = int(lens[0])
+    S = cache.cfg.max_seq
+    pats = _logit_patterns(n, np.random.default_rng(5))
+    names = sorted(pats)
+    bufs = kvq.DecodeBuffers(cache)
+    vds = {}
+    for rot in range(len(names)):
+        la = np.zeros((wl.batch, wl.n_q_heads, S), np.float32)
+        for hq in range(wl.n_q_heads):
+            la[0, hq, :n] = pats[names[(rot + hq) % len(names)]].astype(np.float32)
+        bufs.logits.copy_(torch.from_numpy(la).cuda())
+        bufs.out.fill_(float("nan"))
+        kvq.pv_matvec(cache, bufs.logits, bufs.out, bufs.workspace)
+        torch.cuda.synchronize()
+        got = bufs.out.cpu().numpy()
+        for hq in range(wl.n_q_heads):
+            h = hq // wl.group
+            c = case.oracle_stream(0, h)
+            if h not in vds:
+                vds[h] = oracle.dequant_values(c.v_codes, c.v_idx, c.v_val, c.v_scale, case.cbv)
+            l64 = la[0, hq, :n].astype(np.float64)
+            ref = oracle.attend(l64, vds[h])
+            scale = oracle.output_tolerance_scale(l64, c, case.cbv)
+            assert_out_close(got[0, hq], ref, scale,
+                             what=f"{name} pattern={names[(rot + hq) % len(names)]} hq={hq}")
+        assert np.all(got[1] == 0.0), f"{name}: empty sequence output not zero"
