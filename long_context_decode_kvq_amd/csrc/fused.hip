@@ -83,7 +83,13 @@ __global__ __launch_bounds__(kFuseThreads) void fused_decode_kernel(QkArgs a, Pv
   const int n_super = (n_tiles + kFuseWaves - 1) / kFuseWaves;
   const int s_lo = blockIdx.x * a.tiles_per_wave;  // super-tiles per block, set by the launcher
   const int s_hi = min(s_lo + a.tiles_per_wave, n_super);
-  if (s_lo >= s_hi) return;  // block-uniform; the combine reads only parts that hold tokens
+  if (s_lo >= s_hi) {  // block-uniform: an empty part (m = -inf), as the combine reads every part
+    if (threadIdx.x < kHeadDim + 2) {
+      float* dst = pa.partial + ((static_cast<size_t>(seq) * a.n_q_heads + kvh) * pa.n_parts + blockIdx.x) * (kHeadDim + 2);
+      dst[threadIdx.x] = threadIdx.x == kHeadDim ? -INFINITY : 0.0f;
+    }
+    return;
+  }
 
   const size_t stream = static_cast<size_t>(seq) * H + kvh;
   const uint8_t* recs = a.k_codes + stream * S * (16 * KB);
@@ -462,7 +468,6 @@ hipError_t launch_fused_t(int batch, const QkArgs& a0, const PvArgs& p0, hipStre
   a.tiles_per_wave = static_cast<int>((supers + per_stream - 1) / per_stream);  // super-tiles per block
   const int n_blocks = (supers + a.tiles_per_wave - 1) / a.tiles_per_wave;
   pa.n_parts = n_blocks;
-  pa.tiles_per_block = a.tiles_per_wave * kFuseWaves;  // the combine's count of parts holding tokens
   dim3 grid(n_blocks, a.n_kv_heads, batch);
   hipLaunchKernelGGL((fused_decode_kernel<KB, VB>), grid, dim3(kFuseThreads), lds, st, a, pa);
   hipError_t e = hipGetLastError();

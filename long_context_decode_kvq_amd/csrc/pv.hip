@@ -536,9 +536,9 @@ __global__ __launch_bounds__(256) void pv_combine_kernel(PvArgs a) {
   const int seq = blockIdx.y;
   const size_t part_stride = kHeadDim + 2;
   const float* src = a.partial + (static_cast<size_t>(seq) * a.n_q_heads + h) * a.n_parts * part_stride;
-  const int L = min(a.seq_len[seq] & kLenMask, a.max_len);
-  const int n_tiles = (L + kTile - 1) / kTile;
-  const int np = min(a.n_parts, (n_tiles + a.tiles_per_block - 1) / a.tiles_per_block);
+  // Every block of the partial pass writes its part (m = -inf for a block past the
+  // sequence's length), so all n_parts parts are read without waiting for the length.
+  const int np = a.n_parts;
 
   float mj[kCombineRegs], lj[kCombineRegs], oj[kCombineRegs];
 #pragma unroll
